@@ -1,0 +1,474 @@
+/*
+ * CPU oracle for the neighbour-graph attention hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file defines what the path computes, in
+ * plain, slow, obviously correct C with fp64 arithmetic.  Only the tests,
+ * the package's smoke check and the benchmark's CPU-baseline leg may load
+ * it; the GPU library never does, and the two share no code.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P1] deepmd-kit issue "perf: DPA4 .pt2 LAMMPS (C++ AOTI) inference 3-6x
+ *        slower than Python (ASE) due to CPU-side edge construction and data
+ *        marshalling".
+ *   [P2] deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than
+ *        dense and OOM-prone -- move to block-dense attention via the
+ *        destination CSR".
+ *
+ * Readings taken where the pages are silent (each is listed with its reason
+ * in the design notes of the repository):
+ *   - all periodic images within rcut are neighbours, not only the minimum
+ *     image (the diamond boxes of [P2] "Measurements" are smaller than
+ *     2*rcut); the image shift n is stored per edge and the edge vector is
+ *     d = (x_j - x_i) + n*L, neighbour image minus centre;
+ *   - the distance is r2 = (dx*dx + dy*dy) + dz*dz in IEEE fp64 with no
+ *     fused multiply-add, and the cutoff test is strict, r2 < rcut*rcut;
+ *   - a row keeps the sel nearest neighbours, ordered by the total key
+ *     (r2, j, n_x, n_y, n_z) ascending; a row with fewer neighbours within
+ *     rcut is shorter (ragged), never filled past rcut;
+ *   - attention heads are contiguous column blocks of width d = c/H, the
+ *     score scale is 1/sqrt(d), each query attends to every edge of its
+ *     centre including itself, and there are no biases, residuals or norms;
+ *     stacked layers compose, x <- y.
+ *
+ * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Neighbour list: brute force over every atom and every periodic image.     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    double r2;
+    int32_t j;
+    int32_t n[3];
+    double d[3];
+} orc_cand;
+
+/* Total order of [P2] "Proposed fix" rows: nearest first, ties by neighbour
+ * index, then by image shift. */
+static int orc_cand_cmp(const void* pa, const void* pb)
+{
+    const orc_cand* a = (const orc_cand*)pa;
+    const orc_cand* b = (const orc_cand*)pb;
+    if (a->r2 < b->r2) return -1;
+    if (a->r2 > b->r2) return 1;
+    if (a->j != b->j) return a->j < b->j ? -1 : 1;
+    for (int t = 0; t < 3; ++t)
+        if (a->n[t] != b->n[t]) return a->n[t] < b->n[t] ? -1 : 1;
+    return 0;
+}
+
+/* Number of images to try per side along one axis: every image with
+ * |n| * L < rcut + L is reachable, so |n| <= floor(rcut / L) + 1 suffices. */
+static int orc_image_range(double rcut, double side)
+{
+    return (int)floor(rcut / side) + 1;
+}
+
+/*
+ * One centre's neighbour row ([P1] "Root cause analysis": the edge list of
+ * the periodic system; [P2] "Proposed fix": one destination row per centre).
+ *
+ * Every atom j and every image n in [-K, K]^3 is tried; the self pair
+ * (j == i, n == 0) is skipped.  Kept candidates are sorted by the total key
+ * and the first min(sel, count) are returned.  Returns the number written;
+ * *n_within receives the number within rcut before truncation.  Returns -1
+ * if out of memory.  col: [sel], shift: [sel][3], vec: [sel][3] (nullable),
+ * r2out: [sel] (nullable).
+ */
+int64_t orc_nl_row(const double* pos, int64_t n_atoms, const double* box, double rcut,
+                   int32_t sel, int64_t i, int32_t* col, int32_t* shift, double* vec,
+                   double* r2out, int64_t* n_within)
+{
+    const double rc2 = rcut * rcut;
+    int K[3];
+    for (int a = 0; a < 3; ++a) K[a] = orc_image_range(rcut, box[a]);
+
+    size_t cap = 256, cnt = 0;
+    orc_cand* cand = (orc_cand*)malloc(cap * sizeof(orc_cand));
+    if (!cand) return -1;
+
+    const double* xi = pos + 3 * i;
+    for (int64_t j = 0; j < n_atoms; ++j) {
+        const double* xj = pos + 3 * j;
+        for (int nx = -K[0]; nx <= K[0]; ++nx)
+            for (int ny = -K[1]; ny <= K[1]; ++ny)
+                for (int nz = -K[2]; nz <= K[2]; ++nz) {
+                    if (j == i && nx == 0 && ny == 0 && nz == 0) continue;
+                    const int nn[3] = {nx, ny, nz};
+                    double d[3];
+                    for (int a = 0; a < 3; ++a)
+                        d[a] = (xj[a] - xi[a]) + (double)nn[a] * box[a];
+                    double sxy = d[0] * d[0] + d[1] * d[1];
+                    double r2 = sxy + d[2] * d[2];
+                    if (!(r2 < rc2)) continue;
+                    if (cnt == cap) {
+                        cap *= 2;
+                        orc_cand* grown = (orc_cand*)realloc(cand, cap * sizeof(orc_cand));
+                        if (!grown) { free(cand); return -1; }
+                        cand = grown;
+                    }
+                    orc_cand* c = &cand[cnt++];
+                    c->r2 = r2;
+                    c->j = (int32_t)j;
+                    for (int a = 0; a < 3; ++a) { c->n[a] = nn[a]; c->d[a] = d[a]; }
+                }
+    }
+    qsort(cand, cnt, sizeof(orc_cand), orc_cand_cmp);
+    int64_t keep = (int64_t)cnt < (int64_t)sel ? (int64_t)cnt : (int64_t)sel;
+    for (int64_t k = 0; k < keep; ++k) {
+        col[k] = cand[k].j;
+        for (int a = 0; a < 3; ++a) {
+            shift[3 * k + a] = cand[k].n[a];
+            if (vec) vec[3 * k + a] = cand[k].d[a];
+        }
+        if (r2out) r2out[k] = cand[k].r2;
+    }
+    if (n_within) *n_within = (int64_t)cnt;
+    free(cand);
+    return keep;
+}
+
+/*
+ * Whole destination CSR for all centres: row_ptr[n_atoms+1], col[e_cap],
+ * shift[e_cap][3], vec[e_cap][3] (nullable).  Returns E, or -1 if E would
+ * exceed e_cap or memory runs out.  Rows are built independently (OpenMP
+ * over centres) into padded scratch and then concatenated in centre order.
+ */
+int64_t orc_nl_full(const double* pos, int64_t n_atoms, const double* box, double rcut,
+                    int32_t sel, int64_t* row_ptr, int32_t* col, int32_t* shift, double* vec,
+                    int64_t e_cap)
+{
+    int32_t* pcol = (int32_t*)malloc((size_t)n_atoms * sel * sizeof(int32_t));
+    int32_t* pshift = (int32_t*)malloc((size_t)n_atoms * sel * 3 * sizeof(int32_t));
+    double* pvec = (double*)malloc((size_t)n_atoms * sel * 3 * sizeof(double));
+    int64_t* cnt = (int64_t*)malloc((size_t)n_atoms * sizeof(int64_t));
+    int failed = 0;
+    if (!pcol || !pshift || !pvec || !cnt) failed = 1;
+    if (!failed) {
+#pragma omp parallel for schedule(dynamic, 4) reduction(| : failed)
+        for (int64_t i = 0; i < n_atoms; ++i) {
+            int64_t k = orc_nl_row(pos, n_atoms, box, rcut, sel, i, pcol + (size_t)i * sel,
+                                   pshift + (size_t)i * sel * 3, pvec + (size_t)i * sel * 3,
+                                   NULL, NULL);
+            if (k < 0) failed = 1;
+            cnt[i] = k < 0 ? 0 : k;
+        }
+    }
+    int64_t e = 0;
+    if (!failed) {
+        row_ptr[0] = 0;
+        for (int64_t i = 0; i < n_atoms; ++i) row_ptr[i + 1] = row_ptr[i] + cnt[i];
+        e = row_ptr[n_atoms];
+        if (e > e_cap) failed = 1;
+    }
+    if (!failed) {
+        for (int64_t i = 0; i < n_atoms; ++i) {
+            int64_t base = row_ptr[i];
+            for (int64_t k = 0; k < cnt[i]; ++k) {
+                col[base + k] = pcol[(size_t)i * sel + k];
+                for (int a = 0; a < 3; ++a) {
+                    shift[3 * (base + k) + a] = pshift[((size_t)i * sel + k) * 3 + a];
+                    if (vec) vec[3 * (base + k) + a] = pvec[((size_t)i * sel + k) * 3 + a];
+                }
+            }
+        }
+    }
+    free(pcol); free(pshift); free(pvec); free(cnt);
+    return failed ? -1 : e;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention: naive loops, one centre at a time.                             */
+/* ------------------------------------------------------------------------ */
+
+/* y[n][c] = x[n][c] . W[c][c]  (y = x W, W row-major [c_in][c_out]). */
+static void orc_matmul(const double* x, int64_t n, int32_t c, const double* W, double* y)
+{
+    for (int64_t a = 0; a < n; ++a)
+        for (int32_t u = 0; u < c; ++u) {
+            double s = 0.0;
+            for (int32_t t = 0; t < c; ++t) s += x[a * c + t] * W[(int64_t)t * c + u];
+            y[a * c + u] = s;
+        }
+}
+
+/*
+ * One attention layer on one centre's block X[n][c] -> Y[n][c]
+ * ([P2] "Proposed fix: block-dense attention on the graph": dense attention
+ * math on the per-centre (nnei, c) block; "Graph-native alternatives":
+ * per-center self-attention among the center's edges).
+ *
+ *   q = X Wq, k = X Wk, v = X Wv
+ *   for head h (columns h*d .. h*d+d-1) and query row a:
+ *     s_b = (q_a . k_b)_h / sqrt(d)  for every row b of the block
+ *     m = max_b s_b, p_b = exp(s_b - m), Z = sum_b p_b
+ *     o_a[h cols] = (sum_b p_b v_b[h cols]) / Z
+ *   Y = o Wo
+ * W points at the layer's [4][c][c] weights (q, k, v, o).  scratch holds
+ * 4*n*c + n doubles.
+ */
+static void orc_layer_block(const double* X, int64_t n, int32_t c, int32_t heads,
+                            const double* W, double* Y, double* scratch)
+{
+    const int64_t cc = (int64_t)c * c;
+    const int32_t d = c / heads;
+    const double scale = 1.0 / sqrt((double)d);
+    double* q = scratch;
+    double* k = q + n * c;
+    double* v = k + n * c;
+    double* o = v + n * c;
+    double* s = o + n * c;
+    orc_matmul(X, n, c, W + 0 * cc, q);
+    orc_matmul(X, n, c, W + 1 * cc, k);
+    orc_matmul(X, n, c, W + 2 * cc, v);
+    for (int32_t h = 0; h < heads; ++h) {
+        const int32_t c0 = h * d;
+        for (int64_t a = 0; a < n; ++a) {
+            double m = -INFINITY;
+            for (int64_t b = 0; b < n; ++b) {
+                double dot = 0.0;
+                for (int32_t t = 0; t < d; ++t) dot += q[a * c + c0 + t] * k[b * c + c0 + t];
+                s[b] = dot * scale;
+                if (s[b] > m) m = s[b];
+            }
+            double z = 0.0;
+            for (int64_t b = 0; b < n; ++b) {
+                s[b] = exp(s[b] - m);
+                z += s[b];
+            }
+            for (int32_t t = 0; t < d; ++t) {
+                double acc = 0.0;
+                for (int64_t b = 0; b < n; ++b) acc += s[b] * v[b * c + c0 + t];
+                o[a * c + c0 + t] = acc / z;
+            }
+        }
+    }
+    orc_matmul(o, n, c, W + 3 * cc, Y);
+}
+
+static int64_t orc_edge_of(const int64_t* row_ptr, const int32_t* order, int64_t i, int64_t a)
+{
+    int64_t slot = row_ptr[i] + a;
+    return order ? (int64_t)order[slot] : slot;
+}
+
+static int64_t orc_max_row(const int64_t* row_ptr, int64_t n_centres)
+{
+    int64_t m = 0;
+    for (int64_t i = 0; i < n_centres; ++i) {
+        int64_t n = row_ptr[i + 1] - row_ptr[i];
+        if (n > m) m = n;
+    }
+    return m;
+}
+
+/*
+ * Stacked attention layers over the whole edge axis, layer by layer: each
+ * layer gathers every centre's block through the destination CSR
+ * (row_ptr, optional order permutation), runs orc_layer_block and scatters
+ * the rows back; then x <- y for the next layer.
+ * x, y: [n_edges][c] fp64; w: [layers][4][c][c] fp64.  Returns 0, or -1 on
+ * bad arguments / out of memory.
+ */
+int orc_attn_naive(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                   int64_t n_edges, int32_t c, int32_t heads, int32_t layers,
+                   const double* w, const double* x, double* y)
+{
+    if (c < 1 || heads < 1 || c % heads != 0 || layers < 1) return -1;
+    const int64_t nmax = orc_max_row(row_ptr, n_centres);
+    double* cur = (double*)malloc((size_t)(n_edges > 0 ? n_edges : 1) * c * sizeof(double));
+    if (!cur) return -1;
+    memcpy(cur, x, (size_t)n_edges * c * sizeof(double));
+    int failed = 0;
+    for (int32_t l = 0; l < layers && !failed; ++l) {
+        const double* W = w + (size_t)l * 4 * c * c;
+#pragma omp parallel reduction(| : failed)
+        {
+            double* Xb = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
+            double* Yb = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
+            double* sc = (double*)malloc(((size_t)4 * (nmax + 1) * c + nmax + 1) * sizeof(double));
+            if (!Xb || !Yb || !sc) failed = 1;
+#pragma omp for schedule(dynamic, 8)
+            for (int64_t i = 0; i < n_centres; ++i) {
+                if (failed) continue;
+                int64_t n = row_ptr[i + 1] - row_ptr[i];
+                if (n <= 0) continue;
+                for (int64_t a = 0; a < n; ++a)
+                    memcpy(Xb + a * c, cur + orc_edge_of(row_ptr, order, i, a) * c,
+                           (size_t)c * sizeof(double));
+                orc_layer_block(Xb, n, c, heads, W, Yb, sc);
+                for (int64_t a = 0; a < n; ++a)
+                    memcpy(y + orc_edge_of(row_ptr, order, i, a) * c, Yb + a * c,
+                           (size_t)c * sizeof(double));
+            }
+            free(Xb); free(Yb); free(sc);
+        }
+        if (l + 1 < layers) memcpy(cur, y, (size_t)n_edges * c * sizeof(double));
+    }
+    free(cur);
+    return failed ? -1 : 0;
+}
+
+/*
+ * The same stacked layers for a chosen list of centres only.  An edge
+ * belongs to exactly one destination row and a centre's attention reads only
+ * its own rows, so each listed centre can be carried through all layers on
+ * its own.  Only the rows of the listed centres are written to y.
+ */
+int orc_attn_naive_centres(const int64_t* row_ptr, const int32_t* order,
+                           const int64_t* centres, int64_t n_list, int32_t c, int32_t heads,
+                           int32_t layers, const double* w, const double* x, double* y)
+{
+    if (c < 1 || heads < 1 || c % heads != 0 || layers < 1) return -1;
+    int failed = 0;
+#pragma omp parallel reduction(| : failed)
+    {
+        double* Xb = NULL; double* Yb = NULL; double* sc = NULL;
+        int64_t have = -1;
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < n_list; ++t) {
+            if (failed) continue;
+            int64_t i = centres[t];
+            int64_t n = row_ptr[i + 1] - row_ptr[i];
+            if (n <= 0) continue;
+            if (n > have) {
+                free(Xb); free(Yb); free(sc);
+                Xb = (double*)malloc((size_t)n * c * sizeof(double));
+                Yb = (double*)malloc((size_t)n * c * sizeof(double));
+                sc = (double*)malloc(((size_t)4 * n * c + n) * sizeof(double));
+                have = n;
+                if (!Xb || !Yb || !sc) { failed = 1; have = -1; continue; }
+            }
+            for (int64_t a = 0; a < n; ++a)
+                memcpy(Xb + a * c, x + orc_edge_of(row_ptr, order, i, a) * c,
+                       (size_t)c * sizeof(double));
+            for (int32_t l = 0; l < layers; ++l) {
+                orc_layer_block(Xb, n, c, heads, w + (size_t)l * 4 * c * c, Yb, sc);
+                memcpy(Xb, Yb, (size_t)n * c * sizeof(double));
+            }
+            for (int64_t a = 0; a < n; ++a)
+                memcpy(y + orc_edge_of(row_ptr, order, i, a) * c, Xb + a * c,
+                       (size_t)c * sizeof(double));
+        }
+        free(Xb); free(Yb); free(sc);
+    }
+    return failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention: the ragged pair-axis form ([P2] "Root cause").                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The same layers computed the way [P2] "Root cause" describes the ragged
+ * route: project every edge, enumerate the P = sum_i n_i^2 (centre, query
+ * edge, key edge) pairs, score each pair per head, take the segment max and
+ * segment sum over the pairs that share a query edge (segment softmax),
+ * normalise each pair's weight, and index_add w_p * v[key edge] into the
+ * query edge's output row; then apply Wo per edge.  Serial, so the
+ * index_add order is fixed.  Returns 0, or -1 on bad arguments / out of
+ * memory.
+ */
+int orc_attn_pairaxis(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                      int64_t n_edges, int32_t c, int32_t heads, int32_t layers,
+                      const double* w, const double* x, double* y)
+{
+    if (c < 1 || heads < 1 || c % heads != 0 || layers < 1) return -1;
+    const int32_t d = c / heads;
+    const double scale = 1.0 / sqrt((double)d);
+    const int64_t cc = (int64_t)c * c;
+    int64_t P = 0;
+    for (int64_t i = 0; i < n_centres; ++i) {
+        int64_t n = row_ptr[i + 1] - row_ptr[i];
+        P += n * n;
+    }
+    const size_t ne = (size_t)(n_edges > 0 ? n_edges : 1);
+    const size_t np = (size_t)(P > 0 ? P : 1);
+    int64_t* qe = (int64_t*)malloc(np * sizeof(int64_t));
+    int64_t* ke = (int64_t*)malloc(np * sizeof(int64_t));
+    double* s = (double*)malloc(np * heads * sizeof(double));
+    double* cur = (double*)malloc(ne * c * sizeof(double));
+    double* q = (double*)malloc(ne * c * sizeof(double));
+    double* k = (double*)malloc(ne * c * sizeof(double));
+    double* v = (double*)malloc(ne * c * sizeof(double));
+    double* out = (double*)malloc(ne * c * sizeof(double));
+    double* segmax = (double*)malloc(ne * heads * sizeof(double));
+    double* segsum = (double*)malloc(ne * heads * sizeof(double));
+    int rc = 0;
+    if (!qe || !ke || !s || !cur || !q || !k || !v || !out || !segmax || !segsum) {
+        rc = -1;
+        goto done;
+    }
+    /* Pair enumeration: p -> (query edge, key edge) of the same centre. */
+    {
+        int64_t p = 0;
+        for (int64_t i = 0; i < n_centres; ++i) {
+            int64_t n = row_ptr[i + 1] - row_ptr[i];
+            for (int64_t a = 0; a < n; ++a)
+                for (int64_t b = 0; b < n; ++b) {
+                    qe[p] = orc_edge_of(row_ptr, order, i, a);
+                    ke[p] = orc_edge_of(row_ptr, order, i, b);
+                    ++p;
+                }
+        }
+    }
+    memcpy(cur, x, (size_t)n_edges * c * sizeof(double));
+    for (int32_t l = 0; l < layers; ++l) {
+        const double* W = w + (size_t)l * 4 * cc;
+        orc_matmul(cur, n_edges, c, W + 0 * cc, q);
+        orc_matmul(cur, n_edges, c, W + 1 * cc, k);
+        orc_matmul(cur, n_edges, c, W + 2 * cc, v);
+        for (int64_t p = 0; p < P; ++p)
+            for (int32_t h = 0; h < heads; ++h) {
+                double dot = 0.0;
+                for (int32_t t = 0; t < d; ++t)
+                    dot += q[qe[p] * c + h * d + t] * k[ke[p] * c + h * d + t];
+                s[p * heads + h] = dot * scale;
+            }
+        for (size_t e = 0; e < (size_t)n_edges * heads; ++e) {
+            segmax[e] = -INFINITY;
+            segsum[e] = 0.0;
+        }
+        for (int64_t p = 0; p < P; ++p)                      /* segment max */
+            for (int32_t h = 0; h < heads; ++h)
+                if (s[p * heads + h] > segmax[qe[p] * heads + h])
+                    segmax[qe[p] * heads + h] = s[p * heads + h];
+        for (int64_t p = 0; p < P; ++p)                      /* exp, segment sum */
+            for (int32_t h = 0; h < heads; ++h) {
+                s[p * heads + h] = exp(s[p * heads + h] - segmax[qe[p] * heads + h]);
+                segsum[qe[p] * heads + h] += s[p * heads + h];
+            }
+        memset(out, 0, (size_t)n_edges * c * sizeof(double));
+        for (int64_t p = 0; p < P; ++p)                      /* normalise, index_add */
+            for (int32_t h = 0; h < heads; ++h) {
+                double wp = s[p * heads + h] / segsum[qe[p] * heads + h];
+                for (int32_t t = 0; t < d; ++t)
+                    out[qe[p] * c + h * d + t] += wp * v[ke[p] * c + h * d + t];
+            }
+        orc_matmul(out, n_edges, c, W + 3 * cc, y);
+        if (l + 1 < layers) memcpy(cur, y, (size_t)n_edges * c * sizeof(double));
+    }
+done:
+    free(qe); free(ke); free(s); free(cur); free(q); free(k); free(v); free(out);
+    free(segmax); free(segsum);
+    return rc;
+}
+
+/* Threads the OpenMP loops above use (1 without OpenMP). */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
