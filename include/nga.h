@@ -1,0 +1,208 @@
+/*
+ * nga.h -- C ABI of the neighbour-graph attention library (libnga.so).
+ *
+ * One step of a neighbour-graph interatomic potential's forward hot path on
+ * one MI355X (gfx950) GPU:
+ *
+ *   nl_build            O(N) cell-list neighbour rows under periodic boundaries
+ *   edge_csr            those rows as a destination CSR with image shifts
+ *   block_attn_forward  block-dense multi-head attention through the CSR
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] deepmd-kit issue "perf: DPA4 .pt2 LAMMPS (C++ AOTI) inference 3-6x
+ *        slower than Python (ASE) due to CPU-side edge construction and data
+ *        marshalling".
+ *   [P2] deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than
+ *        dense and OOM-prone -- move to block-dense attention via the
+ *        destination CSR".
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers unless their name starts with h_ (host).
+ *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
+ *     work on that stream and returns; nothing synchronises except where a
+ *     host readback is asked for explicitly (edge_csr's h_n_edges,
+ *     nga_sync_status).  No call allocates or frees memory: the caller owns
+ *     every buffer, including the workspace, sized by the *_workspace_bytes
+ *     queries (pure host arithmetic).  Keeping the data on the GPU from
+ *     positions to outputs, with one optional readback, is what [P1]
+ *     "Root cause analysis" and "Proposed optimizations" ask for.
+ *   - Arguments are checked on the host before any HIP call; a bad argument
+ *     returns NGA_EINVAL (or NGA_EDTYPE / NGA_EWORKSPACE) and enqueues
+ *     nothing.  Errors found by the kernels (a position outside the box, a
+ *     row over capacity, too many edges, an index out of range) set bits in
+ *     a status word at the start of the workspace; the outputs are then
+ *     unspecified, and the error is returned by the next nga_sync_status()
+ *     or by edge_csr's readback on that workspace.
+ *   - A new workspace must be zero-filled once before its first use (the
+ *     status word is cleared only by nga_sync_status / the readback).
+ *     Calls that share a workspace must be ordered on one stream.
+ *   - HIP runtime failures return NGA_EHIP.
+ */
+#ifndef NGA_H
+#define NGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    NGA_OK = 0,
+    NGA_EINVAL = -1,     /* bad argument (host check) */
+    NGA_EBOX = -2,       /* a position is not finite or not in [0, L) (device check) */
+    NGA_EROWCAP = -3,    /* a centre has more than NGA_ROW_CAP neighbours within rcut */
+    NGA_ECAP = -4,       /* the edge count exceeds the caller's capacity */
+    NGA_EDTYPE = -5,     /* unsupported dtype */
+    NGA_EWORKSPACE = -6, /* workspace missing or smaller than the query returned */
+    NGA_EHIP = -7,       /* HIP runtime error */
+    NGA_EINDEX = -8      /* an index in device data is out of range */
+};
+
+enum { NGA_F64 = 0, NGA_F32 = 1 };
+
+/* Neighbours within rcut that nl_build can rank for one centre. */
+#define NGA_ROW_CAP 512
+
+/* ------------------------------------------------------------------------ */
+/* Neighbour list                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes nl_build needs for n_atoms atoms in the box h_box[3] with
+ * cutoff rcut; 0 if the arguments are invalid. */
+size_t nl_build_workspace_bytes(int64_t n_atoms, const double* h_box, double rcut);
+
+/*
+ * Nearest-sel neighbour rows of every atom under periodic boundaries
+ * ([P1] "Root cause analysis": the GPU O(N) cell list of the Python path;
+ * [P2] "Measurements": nsel nearest within rcut).
+ *
+ * pos       [n_atoms][3] fp64, orthorhombic box h_box[3] (x, y, z side
+ *           lengths, host), periodic on all axes, every component in [0, L).
+ * rcut      cutoff; a neighbour j seen through image n (n in Z^3) is kept if
+ *           r2 < rcut*rcut, where d = (x_j - x_i) + n*L per axis and
+ *           r2 = (dx*dx + dy*dy) + dz*dz in fp64 without fused multiply-add.
+ *           Every image within rcut counts, so boxes smaller than 2*rcut
+ *           are allowed (an atom may neighbour itself through n != 0).
+ * sel       row width; each row keeps the min(sel, count) smallest keys
+ *           (r2, j, n_x, n_y, n_z), ascending, left-packed.
+ * nbr       [n_atoms][sel] int32 out: neighbour index j, -1 past the row end.
+ * nbr_shift [n_atoms][sel][3] int32 out: image shift n, 0 past the row end.
+ * nnei      [n_atoms] int32 out: row length.
+ * Limits (else NGA_EINVAL): n_atoms < 2^31; every box side at least rcut/5
+ * (image shifts |n| <= 5).  At most NGA_ROW_CAP neighbours within rcut per
+ * centre (else NGA_EROWCAP).
+ * Device-detected: NGA_EBOX (position outside [0, L) or not finite),
+ * NGA_EROWCAP.
+ */
+int nl_build(const double* pos, int64_t n_atoms, const double* h_box, double rcut, int32_t sel,
+             int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, size_t ws_bytes,
+             void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Destination CSR                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes edge_csr needs. */
+size_t edge_csr_workspace_bytes(int64_t n_atoms, int32_t sel);
+
+/*
+ * Compact padded neighbour rows into the destination CSR
+ * ([P1] comments: edge_index, edge_vec, edge_scatter_index, edge_mask built
+ * on the device instead of by CPU loops; [P2] "Proposed fix": the
+ * destination CSR, destination_row_ptr).
+ *
+ * nbr, nbr_shift  [n_atoms][sel], [n_atoms][sel][3] int32: nl_build's
+ *                 output, or any padded list.  Slot order is kept.
+ * nnei            [n_atoms] int32 or NULL.  When given, the first
+ *                 min(nnei[i], sel) slots of row i are its edges (a
+ *                 left-packed list) and must hold indices in [0, n_atoms)
+ *                 (else NGA_EINDEX).  When NULL, slot k of row i is an edge
+ *                 iff nbr >= 0 (the edge mask).
+ * pos, h_box      only read when edge_vec != NULL (fp64 [n_atoms][3], host [3]).
+ * row_ptr         [n_atoms+1] int64 out: edges of centre i are
+ *                 row_ptr[i] .. row_ptr[i+1]-1 (destination_row_ptr).
+ * col             [e_cap] int32 out: source atom j of each edge (edge_index).
+ * shift           [e_cap][3] int32 out: image shift n of each edge.
+ * dst             [e_cap] int32 out or NULL: centre i of each edge
+ *                 (edge_scatter_index).
+ * edge_vec        [e_cap][3] fp64 out or NULL: d = (x_j - x_i) + n*L,
+ *                 same formula as nl_build.
+ * e_cap           edge capacity of the outputs; n_atoms*sel always suffices.
+ * h_n_edges       host int64* or NULL.  When given, the call synchronises
+ *                 the stream, stores E there, and returns (and clears) any
+ *                 device error recorded in this workspace.
+ * Device-detected: NGA_ECAP (E > e_cap; only edges below e_cap are written),
+ * NGA_EINDEX (an edge's nbr outside [0, n_atoms)).
+ */
+int edge_csr(const int32_t* nbr, const int32_t* nbr_shift, const int32_t* nnei, int64_t n_atoms,
+             int32_t sel, const double* pos, const double* h_box, int64_t* row_ptr,
+             int32_t* col, int32_t* shift, int32_t* dst, double* edge_vec, int64_t e_cap,
+             int64_t* h_n_edges, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Block-dense neighbour attention                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes block_attn_forward needs for these shapes. */
+size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t nnei_cap, int32_t c,
+                                  int32_t n_heads, int32_t n_layers);
+
+/*
+ * Stacked multi-head self-attention among each centre's edges, gathered
+ * through the destination CSR and scattered back to the edge axis
+ * ([P2] "Proposed fix: block-dense attention on the graph"; "Graph-native
+ * alternatives": per-center self-attention among the center's edges,
+ * destination_row_ptr as the segment offsets).
+ *
+ * For each layer l with weights (Wq, Wk, Wv, Wo) and each centre i with
+ * n = row_ptr[i+1] - row_ptr[i] edges e_0 .. e_{n-1}
+ * (e_a = order ? order[row_ptr[i] + a] : row_ptr[i] + a):
+ *   X = rows x[e_a];  Q = X Wq, K = X Wk, V = X Wv
+ *   head h = columns h*d .. h*d+d-1 (d = c / n_heads):
+ *     P = softmax over the n keys of (Q_h K_h^T / sqrt(d)), row by row
+ *     O_h = P V_h
+ *   rows y[e_a] = [O_0 .. O_{H-1}] Wo
+ * and the next layer reads y.  Every query attends to every edge of its
+ * centre, itself included; there are no biases.
+ *
+ * dtype      NGA_F64 or NGA_F32; x, y and weights share it.
+ * row_ptr    [n_centres+1] int64, row_ptr[0] = 0, non-decreasing.
+ * order      [row_ptr[n_centres]] int32 permutation of the edge rows, or
+ *            NULL (edges already in destination order, as edge_csr
+ *            produces them).
+ * n_edges    rows of x and y; row_ptr[n_centres] must not exceed it.
+ * nnei_cap   upper bound on any row length (sel); sizes the tiles.
+ * weights    [n_layers][4][c][c], matrices q, k, v, o, each row-major
+ *            [c_in][c_out] (y = x W).
+ * x, y       [n_edges][c]; must not alias.  Rows of y that belong to no
+ *            centre are left untouched.
+ * Device-detected: NGA_ECAP (row_ptr[n_centres] > n_edges or a row longer
+ * than nnei_cap; such rows are skipped), NGA_EINDEX (order out of range).
+ */
+int block_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
+                       int64_t n_centres, int64_t n_edges, int32_t nnei_cap, int32_t c,
+                       int32_t n_heads, int32_t n_layers, const void* weights, const void* x,
+                       void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Status                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Synchronise `stream`, then return and clear the first device error
+ * recorded in the workspace `ws` (NGA_OK if none). */
+int nga_sync_status(void* ws, void* stream);
+
+/* Static description of a status code. */
+const char* nga_strerror(int status);
+
+/* Name of the attention kernel block_attn_forward would launch for these
+ * shapes ("fused_f32_d16", "generic", ...), for reporting; never NULL. */
+const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NGA_H */

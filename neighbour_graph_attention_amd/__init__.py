@@ -1,0 +1,31 @@
+"""Neighbour-graph attention hot path on MI355X (gfx950).
+
+Python face of libnga.so, the C-ABI library declared in include/nga.h:
+
+* ``nl_build``: O(N) cell-list neighbour rows under periodic boundaries;
+* ``edge_csr``: those rows as a destination CSR with image shifts;
+* ``block_attn_forward``: block-dense multi-head attention through the CSR.
+
+Importing the package loads the library and fails loudly if it has not been
+built (``neighbour_graph_attention_amd._build.build()``).
+"""
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    NGA_F32,
+    NGA_F64,
+    ROW_CAP,
+    NGAError,
+    Workspace,
+    attn_variant,
+    block_attn_forward,
+    block_attn_workspace_bytes,
+    check_status,
+    edge_csr,
+    load,
+    nl_build,
+    nl_build_workspace_bytes,
+    strerror,
+    sync_status,
+)
+
+load()

@@ -1,0 +1,278 @@
+"""ctypes binding of libnga.so (the C ABI declared in include/nga.h).
+
+Argument marshalling only: tensors are checked for dtype, shape, device and
+contiguity, outputs and workspaces are allocated with torch when the caller
+does not pass them, and the raw device pointers plus torch's current HIP
+stream go to the library.  Every step of the computation runs in the
+library's HIP kernels; there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnga.so")
+
+NGA_OK, NGA_EINVAL, NGA_EBOX, NGA_EROWCAP, NGA_ECAP, NGA_EDTYPE, NGA_EWORKSPACE, NGA_EHIP, \
+    NGA_EINDEX = 0, -1, -2, -3, -4, -5, -6, -7, -8
+NGA_F64, NGA_F32 = 0, 1
+ROW_CAP = 512
+
+EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "edge_csr",
+           "block_attn_workspace_bytes", "block_attn_forward", "nga_sync_status", "nga_strerror",
+           "nga_attn_variant")
+
+
+class NGAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (status {code})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libnga.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with neighbour_graph_attention_amd._build")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, dbl, vp, sz = (ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
+                             ctypes.c_size_t)
+    lib.nl_build_workspace_bytes.restype = sz
+    lib.nl_build_workspace_bytes.argtypes = [i64, vp, dbl]
+    lib.nl_build.restype = ctypes.c_int
+    lib.nl_build.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, vp, sz, vp]
+    lib.edge_csr_workspace_bytes.restype = sz
+    lib.edge_csr_workspace_bytes.argtypes = [i64, i32]
+    lib.edge_csr.restype = ctypes.c_int
+    lib.edge_csr.argtypes = [vp, vp, vp, i64, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, sz, vp]
+    lib.block_attn_workspace_bytes.restype = sz
+    lib.block_attn_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32, i32]
+    lib.block_attn_forward.restype = ctypes.c_int
+    lib.block_attn_forward.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp,
+                                       vp, vp, sz, vp]
+    lib.nga_sync_status.restype = ctypes.c_int
+    lib.nga_sync_status.argtypes = [vp, vp]
+    lib.nga_strerror.restype = ctypes.c_char_p
+    lib.nga_strerror.argtypes = [ctypes.c_int]
+    lib.nga_attn_variant.restype = ctypes.c_char_p
+    lib.nga_attn_variant.argtypes = [ctypes.c_int, i32, i32, i32]
+    _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load().nga_strerror(int(code)).decode()
+
+
+def _check(code: int, where: str) -> None:
+    if code != NGA_OK:
+        raise NGAError(code, where)
+
+
+def _box3(box) -> ctypes.Array:
+    vals = [float(v) for v in box]
+    if len(vals) != 3:
+        raise ValueError("box must have 3 side lengths")
+    return (ctypes.c_double * 3)(*vals)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+class Workspace:
+    """A zero-filled device byte buffer, grown on demand, holding the status word."""
+
+    def __init__(self, device, nbytes: int = 256):
+        self.device = torch.device(device)
+        self.buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=self.device)
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+    def ensure(self, nbytes: int) -> "Workspace":
+        if nbytes > self.nbytes:
+            torch.cuda.current_stream(self.device).synchronize()
+            self.buf = torch.zeros(int(nbytes), dtype=torch.uint8, device=self.device)
+        return self
+
+    def ptr(self):
+        return ctypes.c_void_p(self.buf.data_ptr())
+
+
+def _ws(ws, device, nbytes):
+    if ws is None:
+        ws = Workspace(device, nbytes)
+    return ws.ensure(nbytes)
+
+
+def sync_status(ws: Workspace) -> int:
+    """Synchronise the current stream, return and clear the workspace's device error."""
+    return int(load().nga_sync_status(ws.ptr(), _stream(ws.device)))
+
+
+def check_status(ws: Workspace, where: str = "nga") -> None:
+    _check(sync_status(ws), where)
+
+
+def nl_build_workspace_bytes(n_atoms: int, box, rcut: float) -> int:
+    return int(load().nl_build_workspace_bytes(int(n_atoms), _box3(box), float(rcut)))
+
+
+def nl_build(pos: torch.Tensor, box, rcut: float, sel: int, *, nbr=None, nbr_shift=None,
+             nnei=None, ws: Workspace | None = None):
+    """Neighbour rows: returns (nbr [N][sel] int32, nbr_shift [N][sel][3] int32, nnei [N] int32)."""
+    lib = load()
+    dev = pos.device
+    n = pos.shape[0]
+    _need(pos, "pos", torch.float64, (n, 3), dev)
+    nbytes = nl_build_workspace_bytes(n, box, rcut)
+    if nbytes == 0:
+        raise NGAError(NGA_EINVAL, "nl_build_workspace_bytes")
+    ws = _ws(ws, dev, nbytes)
+    if nbr is None:
+        nbr = torch.empty((n, sel), dtype=torch.int32, device=dev)
+    if nbr_shift is None:
+        nbr_shift = torch.empty((n, sel, 3), dtype=torch.int32, device=dev)
+    if nnei is None:
+        nnei = torch.empty((n,), dtype=torch.int32, device=dev)
+    _need(nbr, "nbr", torch.int32, (n, sel), dev)
+    _need(nbr_shift, "nbr_shift", torch.int32, (n, sel, 3), dev)
+    _need(nnei, "nnei", torch.int32, (n,), dev)
+    rc = lib.nl_build(_ptr(pos), n, _box3(box), float(rcut), int(sel), _ptr(nbr), _ptr(nbr_shift),
+                      _ptr(nnei), ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "nl_build")
+    return nbr, nbr_shift, nnei
+
+
+def edge_csr(nbr: torch.Tensor, nbr_shift: torch.Tensor, nnei: torch.Tensor | None = None, *,
+             pos: torch.Tensor | None = None, box=None, e_cap: int | None = None,
+             want_dst: bool = True, want_edge_vec: bool = False, read_n_edges: bool = True,
+             out: dict | None = None, ws: Workspace | None = None):
+    """Destination CSR.  Returns a dict with row_ptr, col, shift, dst, edge_vec, n_edges.
+
+    With read_n_edges (default) the call synchronises once and the edge arrays are trimmed
+    to E; otherwise they keep e_cap rows and n_edges is None.
+    """
+    lib = load()
+    dev = nbr.device
+    n, sel = nbr.shape
+    _need(nbr, "nbr", torch.int32, (n, sel), dev)
+    _need(nbr_shift, "nbr_shift", torch.int32, (n, sel, 3), dev)
+    if nnei is not None:
+        _need(nnei, "nnei", torch.int32, (n,), dev)
+    if e_cap is None:
+        e_cap = n * sel
+    o = dict(out or {})
+    if "row_ptr" not in o:
+        o["row_ptr"] = torch.empty((n + 1,), dtype=torch.int64, device=dev)
+    if "col" not in o:
+        o["col"] = torch.empty((e_cap,), dtype=torch.int32, device=dev)
+    if "shift" not in o:
+        o["shift"] = torch.empty((e_cap, 3), dtype=torch.int32, device=dev)
+    if want_dst and "dst" not in o:
+        o["dst"] = torch.empty((e_cap,), dtype=torch.int32, device=dev)
+    if want_edge_vec and "edge_vec" not in o:
+        o["edge_vec"] = torch.empty((e_cap, 3), dtype=torch.float64, device=dev)
+    _need(o["row_ptr"], "row_ptr", torch.int64, (n + 1,), dev)
+    _need(o["col"], "col", torch.int32, (e_cap,), dev)
+    _need(o["shift"], "shift", torch.int32, (e_cap, 3), dev)
+    dst = o.get("dst") if want_dst else None
+    ev = o.get("edge_vec") if want_edge_vec else None
+    if dst is not None:
+        _need(dst, "dst", torch.int32, (e_cap,), dev)
+    boxp = None
+    if ev is not None:
+        _need(ev, "edge_vec", torch.float64, (e_cap, 3), dev)
+        _need(pos, "pos", torch.float64, (n, 3), dev)
+        boxp = _box3(box)
+    ws = _ws(ws, dev, int(lib.edge_csr_workspace_bytes(n, sel)))
+    ne = ctypes.c_int64(-1)
+    rc = lib.edge_csr(_ptr(nbr), _ptr(nbr_shift), _ptr(nnei), n, sel,
+                      _ptr(pos) if ev is not None else None, boxp, _ptr(o["row_ptr"]),
+                      _ptr(o["col"]), _ptr(o["shift"]), _ptr(dst), _ptr(ev), int(e_cap),
+                      ctypes.byref(ne) if read_n_edges else None, ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "edge_csr")
+    res = {"row_ptr": o["row_ptr"], "col": o["col"], "shift": o["shift"], "dst": dst,
+           "edge_vec": ev, "n_edges": None, "ws": ws}
+    if read_n_edges:
+        e = int(ne.value)
+        res["n_edges"] = e
+        for k in ("col", "shift", "dst", "edge_vec"):
+            if res[k] is not None:
+                res[k] = res[k][:e]
+    return res
+
+
+def _attn_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float64:
+        return NGA_F64
+    if t.dtype == torch.float32:
+        return NGA_F32
+    raise TypeError(f"attention features must be float64 or float32, got {t.dtype}")
+
+
+def block_attn_workspace_bytes(dtype: int, n_edges: int, nnei_cap: int, c: int, n_heads: int,
+                               n_layers: int) -> int:
+    return int(load().block_attn_workspace_bytes(dtype, n_edges, nnei_cap, c, n_heads, n_layers))
+
+
+def attn_variant(dtype: int, nnei_cap: int, c: int, n_heads: int) -> str:
+    return load().nga_attn_variant(dtype, nnei_cap, c, n_heads).decode()
+
+
+def block_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Tensor,
+                       n_heads: int, nnei_cap: int, *, order: torch.Tensor | None = None,
+                       y: torch.Tensor | None = None, ws: Workspace | None = None):
+    """Stacked block-dense attention layers; returns y [E][c] (same dtype as x)."""
+    lib = load()
+    dev = x.device
+    e, c = x.shape
+    dt = _attn_dtype(x)
+    n_centres = row_ptr.shape[0] - 1
+    _need(row_ptr, "row_ptr", torch.int64, (n_centres + 1,), dev)
+    if weights.dim() != 4:
+        raise ValueError("weights must be [layers][4][c][c]")
+    layers = weights.shape[0]
+    _need(weights, "weights", x.dtype, (layers, 4, c, c), dev)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if order is not None:
+        if order.dim() != 1 or order.dtype != torch.int32 or order.device != dev or \
+                not order.is_contiguous():
+            raise ValueError("order must be a contiguous int32 vector on the device")
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, (e, c), dev)
+    ws = _ws(ws, dev, block_attn_workspace_bytes(dt, e, nnei_cap, c, n_heads, layers))
+    rc = lib.block_attn_forward(dt, _ptr(row_ptr), _ptr(order), n_centres, e, int(nnei_cap), c,
+                                int(n_heads), int(layers), _ptr(weights), _ptr(x), _ptr(y),
+                                ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "block_attn_forward")
+    return y

@@ -1,0 +1,352 @@
+// block_attn_forward: block-dense multi-head neighbour attention through the destination CSR.
+//
+// deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than dense and OOM-prone --
+// move to block-dense attention via the destination CSR", section "Proposed fix: block-dense
+// attention on the graph": gather each centre's (nnei, c) block through the destination CSR,
+// run dense attention math with per-row masks for the ragged tail, scatter back to the edge
+// axis, so the P = sum nnei^2 pair axis never exists.  Section "Graph-native alternatives":
+// the attention is self-attention among one centre's edges, destination_row_ptr being the
+// segment offsets.
+//
+// This file holds the host entry point and the path that works for any shape: three
+// kernels per layer over slot-indexed workspace buffers (slot = position in the CSR):
+//   qkv[s]  = x[order(s)] [Wq | Wk | Wv]           (row-gather GEMM)
+//   o[s]    = per-centre attention of qkv rows      (one work-group per centre)
+//   y[order(s)] = o[s] Wo                           (row-scatter GEMM)
+// The fused fp32 kernel for 16-wide heads lives in block_attn_fused.hip.
+#include "nga_internal.h"
+#include "block_attn_fused.h"
+
+namespace nga {
+
+namespace {
+
+constexpr int kGemmBM = 64, kGemmBN = 64, kGemmBK = 16;
+
+template <typename T>
+struct GemmArgs {
+    const T* a;
+    const int32_t* a_rows;  // nullable: row m of A is a[a_rows[m]]
+    const T* w;             // nmat matrices [c][c] side by side in the output columns
+    T* out;
+    const int32_t* out_rows;  // nullable: row m of the result goes to out[out_rows[m]]
+    const int64_t* e_dev;     // rows m < *e_dev are computed
+    int64_t n_edges;          // bound on gathered / scattered row indices
+    int c;
+    int nmat;
+    int lda;
+    int ldo;
+    uint32_t* status;
+};
+
+// out[m][u] = sum_t A[m][t] * W_{u / c}[t][u % c], 64x64 tiles, 4x4 per thread.
+template <typename T>
+__global__ void __launch_bounds__(256) gemm_rows_kernel(GemmArgs<T> g) {
+    __shared__ T sa[kGemmBK][kGemmBM + 1];
+    __shared__ T sw[kGemmBK][kGemmBN + 1];
+    const int64_t E = *g.e_dev < g.n_edges ? *g.e_dev : g.n_edges;
+    const int64_t m0 = (int64_t)blockIdx.x * kGemmBM;
+    const int u0 = blockIdx.y * kGemmBN;
+    if (m0 >= E) return;
+    const int nout = g.nmat * g.c;
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    T acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = T(0);
+    for (int k0 = 0; k0 < g.c; k0 += kGemmBK) {
+        for (int idx = threadIdx.x; idx < kGemmBM * kGemmBK; idx += 256) {
+            int r = idx / kGemmBK, kk = idx % kGemmBK;
+            int64_t m = m0 + r;
+            T v = T(0);
+            if (m < E && k0 + kk < g.c) {
+                int64_t row = g.a_rows ? (int64_t)g.a_rows[m] : m;
+                if (row >= 0 && row < g.n_edges) v = g.a[row * g.lda + k0 + kk];
+            }
+            sa[kk][r] = v;
+        }
+        for (int idx = threadIdx.x; idx < kGemmBK * kGemmBN; idx += 256) {
+            int kk = idx / kGemmBN, cc = idx % kGemmBN;
+            int u = u0 + cc, t = k0 + kk;
+            T v = T(0);
+            if (u < nout && t < g.c) {
+                int mat = u / g.c, col = u % g.c;
+                v = g.w[(int64_t)mat * g.c * g.c + (int64_t)t * g.c + col];
+            }
+            sw[kk][cc] = v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < kGemmBK; ++kk) {
+            T av[4], wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[i] = sa[kk][ty * 4 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wv[j] = sw[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] += av[i] * wv[j];
+        }
+        __syncthreads();
+    }
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        int64_t m = m0 + ty * 4 + i;
+        if (m >= E) continue;
+        int64_t row = m;
+        if (g.a_rows) {
+            int64_t ar = g.a_rows[m];
+            if (ar < 0 || ar >= g.n_edges) bad = true;
+        }
+        if (g.out_rows) {
+            row = g.out_rows[m];
+            if (row < 0 || row >= g.n_edges) { bad = true; continue; }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int u = u0 + tx * 4 + j;
+            if (u < nout) g.out[row * g.ldo + u] = acc[i][j];
+        }
+    }
+    if (bad) raise_bits(g.status, kBitIndex);
+}
+
+template <typename T>
+__device__ inline T exp_t(T v);
+template <>
+__device__ inline double exp_t<double>(double v) { return exp(v); }
+template <>
+__device__ inline float exp_t<float>(float v) { return expf(v); }
+
+template <typename T>
+struct CoreArgs {
+    const T* qkv;  // [E][3c] slot-indexed: q | k | v
+    T* o;          // [E][c] slot-indexed
+    const int64_t* row_ptr;
+    int n_centres;
+    int64_t n_edges;
+    int nnei_cap;
+    int c;
+    int heads;
+    int d;
+    T scale;
+    uint32_t* status;
+};
+
+// One work-group per centre; each thread owns (query row a, head h) pairs and makes two
+// passes over the centre's keys: the row max, then exp / sum / weighted values.
+template <typename T, int DMAX>
+__global__ void __launch_bounds__(256) attn_core_kernel(CoreArgs<T> A) {
+    const int i = blockIdx.x;
+    const int64_t r0 = A.row_ptr[i], r1 = A.row_ptr[i + 1];
+    const int n = (int)(r1 - r0);
+    if (n <= 0) return;
+    if (n > A.nnei_cap || r1 > A.n_edges) {
+        if (threadIdx.x == 0) raise_bits(A.status, kBitCap);
+        return;
+    }
+    const int c = A.c, c3 = 3 * A.c, d = A.d;
+    for (int idx = threadIdx.x; idx < n * A.heads; idx += blockDim.x) {
+        const int a = idx / A.heads, h = idx % A.heads;
+        const T* q = A.qkv + (r0 + a) * c3 + h * d;
+        T qr[DMAX];
+#pragma unroll
+        for (int t = 0; t < DMAX; ++t) qr[t] = t < d ? q[t] : T(0);
+        T m = -INFINITY;
+        for (int b = 0; b < n; ++b) {
+            const T* kb = A.qkv + (r0 + b) * c3 + c + h * d;
+            T s = T(0);
+#pragma unroll
+            for (int t = 0; t < DMAX; ++t)
+                if (t < d) s += qr[t] * kb[t];
+            s *= A.scale;
+            m = s > m ? s : m;
+        }
+        T acc[DMAX];
+#pragma unroll
+        for (int t = 0; t < DMAX; ++t) acc[t] = T(0);
+        T z = T(0);
+        for (int b = 0; b < n; ++b) {
+            const T* kb = A.qkv + (r0 + b) * c3 + c + h * d;
+            const T* vb = A.qkv + (r0 + b) * c3 + 2 * c + h * d;
+            T s = T(0);
+#pragma unroll
+            for (int t = 0; t < DMAX; ++t)
+                if (t < d) s += qr[t] * kb[t];
+            const T p = exp_t<T>(s * A.scale - m);
+            z += p;
+#pragma unroll
+            for (int t = 0; t < DMAX; ++t)
+                if (t < d) acc[t] += p * vb[t];
+        }
+        T* out = A.o + (r0 + a) * c + h * d;
+#pragma unroll
+        for (int t = 0; t < DMAX; ++t)
+            if (t < d) out[t] = acc[t] / z;
+    }
+}
+
+__global__ void check_rows_kernel(const int64_t* row_ptr, int n_centres, int64_t n_edges,
+                                  uint32_t* status) {
+    if (row_ptr[n_centres] > n_edges || row_ptr[0] != 0) raise_bits(status, kBitCap);
+}
+
+struct GenericWs {
+    void* qkv;
+    void* o;
+    void* xbuf;
+    size_t bytes;
+};
+
+GenericWs carve_generic(void* ws, int64_t e, int c, int layers, size_t es) {
+    Carver cv(ws);
+    GenericWs w;
+    w.qkv = cv.take<char>((size_t)e * 3 * c * es);
+    w.o = cv.take<char>((size_t)e * c * es);
+    w.xbuf = cv.take<char>(layers > 1 ? (size_t)e * c * es : 0);
+    w.bytes = cv.off;
+    return w;
+}
+
+template <typename T>
+int launch_core(const CoreArgs<T>& A, hipStream_t s) {
+    dim3 grid((unsigned)A.n_centres), block(256);
+    if (A.d <= 8) hipLaunchKernelGGL((attn_core_kernel<T, 8>), grid, block, 0, s, A);
+    else if (A.d <= 16) hipLaunchKernelGGL((attn_core_kernel<T, 16>), grid, block, 0, s, A);
+    else if (A.d <= 32) hipLaunchKernelGGL((attn_core_kernel<T, 32>), grid, block, 0, s, A);
+    else if (A.d <= 64) hipLaunchKernelGGL((attn_core_kernel<T, 64>), grid, block, 0, s, A);
+    else hipLaunchKernelGGL((attn_core_kernel<T, 128>), grid, block, 0, s, A);
+    return last_launch_status();
+}
+
+template <typename T>
+int launch_gemm(const GemmArgs<T>& g, int64_t m_bound, hipStream_t s) {
+    const int nout = g.nmat * g.c;
+    dim3 grid((unsigned)((m_bound + kGemmBM - 1) / kGemmBM), (unsigned)((nout + kGemmBN - 1) / kGemmBN));
+    hipLaunchKernelGGL((gemm_rows_kernel<T>), grid, dim3(256), 0, s, g);
+    return last_launch_status();
+}
+
+template <typename T>
+int run_generic(const int64_t* row_ptr, const int32_t* order, int64_t n_centres, int64_t n_edges,
+                int32_t nnei_cap, int32_t c, int32_t heads, int32_t layers, const T* weights,
+                const T* x, T* y, void* ws, hipStream_t s) {
+    GenericWs w = carve_generic(ws, n_edges, c, layers, sizeof(T));
+    uint32_t* status = &static_cast<WsHeader*>(ws)->status;
+    const int64_t* e_dev = row_ptr + n_centres;
+    T* qkv = static_cast<T*>(w.qkv);
+    T* o = static_cast<T*>(w.o);
+    T* xbuf = static_cast<T*>(w.xbuf);
+    const int d = c / heads;
+    const size_t cc = (size_t)c * c;
+    int rc;
+    for (int l = 0; l < layers; ++l) {
+        const T* W = weights + (size_t)l * 4 * cc;
+        GemmArgs<T> g1;
+        g1.a = (l == 0) ? x : xbuf;
+        g1.a_rows = (l == 0) ? order : nullptr;
+        g1.w = W;
+        g1.out = qkv;
+        g1.out_rows = nullptr;
+        g1.e_dev = e_dev;
+        g1.n_edges = n_edges;
+        g1.c = c;
+        g1.nmat = 3;
+        g1.lda = c;
+        g1.ldo = 3 * c;
+        g1.status = status;
+        if ((rc = launch_gemm(g1, n_edges, s))) return rc;
+        CoreArgs<T> A;
+        A.qkv = qkv;
+        A.o = o;
+        A.row_ptr = row_ptr;
+        A.n_centres = (int)n_centres;
+        A.n_edges = n_edges;
+        A.nnei_cap = nnei_cap;
+        A.c = c;
+        A.heads = heads;
+        A.d = d;
+        A.scale = T(1) / std::sqrt(T(d));
+        A.status = status;
+        if ((rc = launch_core(A, s))) return rc;
+        GemmArgs<T> g2 = g1;
+        g2.a = o;
+        g2.a_rows = nullptr;
+        g2.w = W + 3 * cc;
+        g2.nmat = 1;
+        g2.lda = c;
+        g2.ldo = c;
+        const bool last = (l == layers - 1);
+        g2.out = last ? y : xbuf;
+        g2.out_rows = last ? order : nullptr;
+        if ((rc = launch_gemm(g2, n_edges, s))) return rc;
+    }
+    return NGA_OK;
+}
+
+bool use_fused(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
+    return fused_supported(dtype, nnei_cap, c, heads);
+}
+
+}  // namespace
+
+}  // namespace nga
+
+extern "C" size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t nnei_cap,
+                                             int32_t c, int32_t n_heads, int32_t n_layers) {
+    if (dtype != NGA_F64 && dtype != NGA_F32) return 0;
+    if (n_edges < 0 || c < 1 || n_heads < 1 || n_layers < 1 || nnei_cap < 1) return 0;
+    if (nga::use_fused(dtype, nnei_cap, c, n_heads)) return nga::align_up(sizeof(nga::WsHeader));
+    const size_t es = dtype == NGA_F64 ? sizeof(double) : sizeof(float);
+    return nga::carve_generic(nullptr, n_edges, c, n_layers, es).bytes;
+}
+
+extern "C" const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads) {
+    if (dtype != NGA_F64 && dtype != NGA_F32) return "unsupported";
+    if (nga::use_fused(dtype, nnei_cap, c, n_heads)) return nga::fused_name(dtype, c, n_heads);
+    return dtype == NGA_F64 ? "generic_f64" : "generic_f32";
+}
+
+extern "C" int block_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
+                                  int64_t n_centres, int64_t n_edges, int32_t nnei_cap,
+                                  int32_t c, int32_t n_heads, int32_t n_layers,
+                                  const void* weights, const void* x, void* y, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    using namespace nga;
+    if (dtype != NGA_F64 && dtype != NGA_F32) return NGA_EDTYPE;
+    if (n_centres < 0 || n_centres >= INT32_MAX || n_edges < 0 || nnei_cap < 1 || c < 1 ||
+        n_heads < 1 || c % n_heads != 0 || n_layers < 1)
+        return NGA_EINVAL;
+    if (c / n_heads > 128) return NGA_EINVAL;
+    if (!row_ptr) return NGA_EINVAL;
+    if (n_edges > 0 && (!x || !y || !weights)) return NGA_EINVAL;
+    const size_t es = dtype == NGA_F64 ? sizeof(double) : sizeof(float);
+    if (n_edges > 0) {
+        const char* xb = static_cast<const char*>(x);
+        const char* yb = static_cast<const char*>(y);
+        const size_t span = (size_t)n_edges * c * es;
+        if (xb < yb + span && yb < xb + span) return NGA_EINVAL;
+    }
+    const size_t need = block_attn_workspace_bytes(dtype, n_edges, nnei_cap, c, n_heads, n_layers);
+    if (!ws || ws_bytes < need) return NGA_EWORKSPACE;
+    if (n_centres == 0 || n_edges == 0) return NGA_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t* status = &static_cast<WsHeader*>(ws)->status;
+    hipLaunchKernelGGL(check_rows_kernel, dim3(1), dim3(1), 0, s, row_ptr, (int)n_centres, n_edges,
+                       status);
+    int rc = last_launch_status();
+    if (rc) return rc;
+    if (use_fused(dtype, nnei_cap, c, n_heads))
+        return run_fused(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
+                         weights, x, y, status, s);
+    if (dtype == NGA_F64)
+        return run_generic<double>(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads,
+                                   n_layers, static_cast<const double*>(weights),
+                                   static_cast<const double*>(x), static_cast<double*>(y), ws, s);
+    return run_generic<float>(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
+                              static_cast<const float*>(weights), static_cast<const float*>(x),
+                              static_cast<float*>(y), ws, s);
+}

@@ -1,0 +1,15 @@
+// Fused per-centre attention kernels (block_attn_fused.hip).
+#pragma once
+
+#include "nga_internal.h"
+
+namespace nga {
+
+// True if a fused kernel covers these shapes.
+bool fused_supported(int dtype, int32_t nnei_cap, int32_t c, int32_t heads);
+const char* fused_name(int dtype, int32_t c, int32_t heads);
+int run_fused(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+              int64_t n_edges, int32_t nnei_cap, int32_t c, int32_t heads, int32_t layers,
+              const void* weights, const void* x, void* y, uint32_t* status, hipStream_t s);
+
+}  // namespace nga

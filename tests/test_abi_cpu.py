@@ -1,0 +1,131 @@
+"""The C-ABI library without a GPU: it loads, exports what include/nga.h declares,
+and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import neighbour_graph_attention_amd as nga
+from neighbour_graph_attention_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "nga.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_expected_functions():
+    assert _declared_functions() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_codes():
+    for code in range(0, -9, -1):
+        assert nga.strerror(code) != "unknown status"
+    assert nga.strerror(-99) == "unknown status"
+
+
+def test_nl_workspace_query():
+    lib = nga.load()
+    box = (ctypes.c_double * 3)(10.0, 10.0, 10.0)
+    assert lib.nl_build_workspace_bytes(100, box, 2.0) > 0
+    assert lib.nl_build_workspace_bytes(100, box, 0.0) == 0
+    assert lib.nl_build_workspace_bytes(100, box, float("nan")) == 0
+    assert lib.nl_build_workspace_bytes(-1, box, 2.0) == 0
+    bad = (ctypes.c_double * 3)(10.0, -1.0, 10.0)
+    assert lib.nl_build_workspace_bytes(100, bad, 2.0) == 0
+    tiny = (ctypes.c_double * 3)(1.0, 1.0, 1.0)
+    assert lib.nl_build_workspace_bytes(10, tiny, 5.5) == 0   # box side below rcut / 5
+    assert lib.nl_build_workspace_bytes(10, tiny, 4.9) > 0
+
+
+def test_nl_build_rejects_bad_arguments():
+    lib = nga.load()
+    box = (ctypes.c_double * 3)(10.0, 10.0, 10.0)
+    big = 1 << 30
+    ok = dict(pos=FAKE, n=10, box=box, rcut=2.0, sel=8, nbr=FAKE, sh=FAKE, nn=FAKE, ws=FAKE,
+              wsb=big)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.nl_build(a["pos"], a["n"], a["box"], a["rcut"], a["sel"], a["nbr"], a["sh"],
+                            a["nn"], a["ws"], a["wsb"], None)
+
+    assert call(rcut=-1.0) == L.NGA_EINVAL
+    assert call(sel=0) == L.NGA_EINVAL
+    assert call(n=-5) == L.NGA_EINVAL
+    assert call(pos=None) == L.NGA_EINVAL
+    assert call(nbr=None) == L.NGA_EINVAL
+    assert call(box=None) == L.NGA_EINVAL
+    assert call(ws=None) == L.NGA_EWORKSPACE
+    assert call(wsb=16) == L.NGA_EWORKSPACE
+    assert call(n=0) == L.NGA_OK  # empty input: nothing to enqueue
+
+
+def test_edge_csr_rejects_bad_arguments():
+    lib = nga.load()
+    box = (ctypes.c_double * 3)(10.0, 10.0, 10.0)
+    big = 1 << 30
+
+    def call(n=10, sel=8, nbr=FAKE, rp=FAKE, col=FAKE, ev=None, pos=None, hb=None, ecap=80,
+             ws=FAKE, wsb=big):
+        return lib.edge_csr(nbr, FAKE, None, n, sel, pos, hb, rp, col, FAKE, None, ev, ecap,
+                            None, ws, wsb, None)
+
+    assert call(sel=0) == L.NGA_EINVAL
+    assert call(n=-1) == L.NGA_EINVAL
+    assert call(rp=None) == L.NGA_EINVAL
+    assert call(nbr=None) == L.NGA_EINVAL
+    assert call(col=None) == L.NGA_EINVAL
+    assert call(ecap=-1) == L.NGA_EINVAL
+    assert call(ev=FAKE) == L.NGA_EINVAL            # edge_vec needs pos and box
+    assert call(ev=FAKE, pos=FAKE, hb=(ctypes.c_double * 3)(1.0, 0.0, 1.0)) == L.NGA_EINVAL
+    assert call(ws=None) == L.NGA_EWORKSPACE
+    assert call(wsb=8) == L.NGA_EWORKSPACE
+    assert lib.edge_csr_workspace_bytes(10, 8) > 0
+    assert lib.edge_csr_workspace_bytes(10, 0) == 0
+    del box
+
+
+def test_block_attn_rejects_bad_arguments():
+    lib = nga.load()
+    big = 1 << 40
+
+    def call(dt=L.NGA_F64, nc=4, ne=40, cap=16, c=16, h=4, layers=1, rp=FAKE, w=FAKE,
+             x=0x100000, y=0x900000, ws=FAKE, wsb=big):
+        return lib.block_attn_forward(dt, rp, None, nc, ne, cap, c, h, layers, w,
+                                      ctypes.c_void_p(x), ctypes.c_void_p(y), ws, wsb, None)
+
+    assert call(dt=7) == L.NGA_EDTYPE
+    assert call(c=18, h=4) == L.NGA_EINVAL           # c not divisible by heads
+    assert call(h=0) == L.NGA_EINVAL
+    assert call(layers=0) == L.NGA_EINVAL
+    assert call(cap=0) == L.NGA_EINVAL
+    assert call(rp=None) == L.NGA_EINVAL
+    assert call(w=None) == L.NGA_EINVAL
+    assert call(c=256, h=1) == L.NGA_EINVAL          # head width above 128
+    assert call(y=0x100000 + 8) == L.NGA_EINVAL      # x and y overlap
+    assert call(ws=None) == L.NGA_EWORKSPACE
+    assert call(wsb=4) == L.NGA_EWORKSPACE
+    assert call(nc=0) == L.NGA_OK                    # nothing to do
+    assert call(ne=0) == L.NGA_OK
+
+
+def test_attention_workspace_and_variant_queries():
+    lib = nga.load()
+    assert lib.block_attn_workspace_bytes(9, 10, 8, 8, 2, 1) == 0
+    g = lib.block_attn_workspace_bytes(L.NGA_F64, 1000, 40, 32, 4, 6)
+    assert g >= 1000 * 32 * 8 * 5
+    assert nga.attn_variant(L.NGA_F64, 40, 32, 4).startswith(("generic", "fused"))
+    assert nga.attn_variant(5, 40, 32, 4) == "unsupported"

@@ -1,0 +1,208 @@
+"""GPU neighbour rows and destination CSR against the oracle: bit-exact.
+
+Whole-CSR comparisons on every input the oracle finishes in seconds (the
+three diamond workloads, ideal lattices with exact distance ties, tiny boxes
+with many images, random orthorhombic boxes, hand cases), sampled rows plus
+whole-list invariants on the two Fe BCC workloads at full size, and the
+device-detected error paths.
+"""
+import numpy as np
+import pytest
+import torch
+
+import neighbour_graph_attention_amd as nga
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _gpu_csr(pos_np, box, rcut, sel, want_vec=True):
+    pos = torch.from_numpy(np.ascontiguousarray(pos_np, dtype=np.float64)).to(DEV)
+    nbr, nbr_shift, nnei = nga.nl_build(pos, box, rcut, sel)
+    csr = nga.edge_csr(nbr, nbr_shift, nnei, pos=pos, box=box, want_edge_vec=want_vec)
+    nga.check_status(csr["ws"], "csr")
+    out = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in csr.items()
+           if k != "ws"}
+    out["nbr"] = nbr.cpu().numpy()
+    out["nbr_shift"] = nbr_shift.cpu().numpy()
+    out["nnei"] = nnei.cpu().numpy()
+    return out
+
+
+def _assert_same_csr(g, ref):
+    rp, col, shift, vec = ref
+    assert np.array_equal(g["row_ptr"], rp)
+    assert np.array_equal(g["col"], col)
+    assert np.array_equal(g["shift"], shift)
+    if g["edge_vec"] is not None:
+        assert np.array_equal(g["edge_vec"], vec)  # bitwise: same fp64 formula, no contraction
+    assert np.array_equal(g["nnei"], np.diff(rp))
+    assert np.array_equal(g["dst"], np.repeat(np.arange(len(rp) - 1), np.diff(rp)))
+
+
+@pytest.mark.parametrize("key", [1, 2, 3])
+def test_diamond_workloads_bitexact(oracle_mod, key):
+    w = W.WORKLOADS[key]
+    pos, box = W.workload_positions(w)
+    print(f"workload {w.name}", flush=True)
+    g = _gpu_csr(pos, box, w.rcut, w.sel)
+    _assert_same_csr(g, oracle_mod.nl_full(pos, box, w.rcut, w.sel))
+    assert g["n_edges"] == pos.shape[0] * w.sel
+
+
+def _row_keys(vec, col, shift):
+    d = vec
+    r2 = (d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]
+    return r2
+
+
+@pytest.mark.parametrize("key", [4, 5])
+def test_fe_bcc_full_size_sampled_rows(oracle_mod, key):
+    """Full-size Fe BCC lists: sampled rows bit-exact vs the oracle, invariants everywhere."""
+    w = W.WORKLOADS[key]
+    pos, box = W.workload_positions(w)
+    n = pos.shape[0]
+    print(f"workload {w.name} N={n}", flush=True)
+    g = _gpu_csr(pos, box, w.rcut, w.sel)
+    rp, col, shift, vec = g["row_ptr"], g["col"], g["shift"], g["edge_vec"]
+    rng = np.random.default_rng(1000 + key)
+    sample = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 40, replace=False)]))
+    for i in sample:
+        c, s, v, r2, nw = oracle_mod.nl_row(pos, box, w.rcut, w.sel, int(i))
+        sl = slice(rp[i], rp[i + 1])
+        assert np.array_equal(col[sl], c), i
+        assert np.array_equal(shift[sl], s), i
+        assert np.array_equal(vec[sl], v), i
+    # invariants over the whole list
+    counts = np.diff(rp)
+    assert counts.max() <= w.sel and counts.min() >= 1
+    r2 = _row_keys(vec, col, shift)
+    assert np.all(r2 < w.rcut * w.rcut)
+    same_row = np.repeat(np.arange(n), counts)
+    nxt = np.arange(len(col) - 1)
+    inrow = same_row[nxt] == same_row[nxt + 1]
+    lo_key = col.astype(np.int64)
+    ordered = (r2[nxt] < r2[nxt + 1]) | ((r2[nxt] == r2[nxt + 1]) & (lo_key[nxt] < lo_key[nxt + 1]))
+    assert np.all(ordered[inrow])
+    # rows are never truncated here, so the relation must be symmetric: (i, j, n) <-> (j, i, -n)
+    assert counts.max() < w.sel
+    code = lambda a, b, s: ((a * n + b) * 1000 + (s[:, 0] + 10) * 100 + (s[:, 1] + 10) * 10
+                            + (s[:, 2] + 10))
+    fwd = np.sort(code(same_row.astype(np.int64), col.astype(np.int64), shift.astype(np.int64)))
+    bwd = np.sort(code(col.astype(np.int64), same_row.astype(np.int64), -shift.astype(np.int64)))
+    assert np.array_equal(fwd, bwd)
+
+
+@pytest.mark.parametrize("lattice,ncells,a,rcut,sel", [
+    ("diamond", 3, W.DIAMOND_A, 6.0, 120),   # 24-way exact tie at the sel boundary
+    ("diamond", 3, W.DIAMOND_A, 6.0, 200),   # untruncated: 158 each
+    ("diamond", 2, W.DIAMOND_A, 6.0, 130),   # rcut > L/2: one cell per axis
+    ("bcc", 4, W.BCC_FE_A, 8.0, 181),        # box 11.5 A: one cell per axis
+    ("bcc", 8, W.BCC_FE_A, 8.0, 100),        # two cells per axis, truncated rows
+    ("fcc", 3, 3.6, 5.0, 60),
+])
+def test_ideal_lattices_bitexact(oracle_mod, lattice, ncells, a, rcut, sel):
+    pos, box = W.make_positions(lattice, ncells, a, 0.0, 0.0, seed=0)
+    g = _gpu_csr(pos, box, rcut, sel)
+    _assert_same_csr(g, oracle_mod.nl_full(pos, box, rcut, sel))
+
+
+@pytest.mark.parametrize("n,box,rcut,sel,seed", [
+    (300, (7.0, 11.0, 23.0), 3.5, 64, 1),
+    (500, (12.0, 12.0, 12.0), 4.0, 20, 2),    # truncated rows
+    (40, (3.0, 4.0, 5.0), 4.5, 300, 3),       # many images, reach 2 on x
+    (1, (1.0, 1.0, 1.0), 2.5, 100, 4),        # one atom, 80 images, reach 3
+    (2, (2.0, 9.0, 2.0), 3.0, 50, 5),
+    (1000, (30.0, 30.0, 30.0), 2.0, 8, 6),    # sparse: many empty cells
+    (700, (40.0, 10.0, 10.0), 2.6, 32, 7),
+])
+def test_random_boxes_bitexact(oracle_mod, n, box, rcut, sel, seed):
+    pos = W.random_positions(n, box, seed)
+    g = _gpu_csr(pos, box, rcut, sel)
+    _assert_same_csr(g, oracle_mod.nl_full(pos, box, rcut, sel))
+
+
+def test_hand_cases(oracle_mod):
+    g = _gpu_csr(np.array([[1.0, 1.0, 1.0], [8.0, 1.0, 1.0]]), (10.0, 10.0, 10.0), 4.0, 4)
+    assert g["row_ptr"].tolist() == [0, 1, 2]
+    assert g["col"].tolist() == [1, 0]
+    assert g["shift"].tolist() == [[-1, 0, 0], [1, 0, 0]]
+    assert g["edge_vec"].tolist() == [[-3.0, 0.0, 0.0], [3.0, 0.0, 0.0]]
+    assert g["nbr"].tolist() == [[1, -1, -1, -1], [0, -1, -1, -1]]
+    g = _gpu_csr(np.array([[1.5, 1.5, 1.5]]), (3.0, 3.0, 3.0), 3.5, 10)
+    assert g["shift"].tolist() == [[-1, 0, 0], [0, -1, 0], [0, 0, -1], [0, 0, 1], [0, 1, 0],
+                                   [1, 0, 0]]
+    # strict cutoff: a neighbour at exactly rcut is excluded
+    g = _gpu_csr(np.array([[1.0, 1.0, 1.0], [3.0, 1.0, 1.0]]), (10.0, 10.0, 10.0), 2.0, 4)
+    assert g["row_ptr"].tolist() == [0, 0, 0]
+
+
+def test_empty_and_single_atom():
+    pos = torch.zeros((0, 3), dtype=torch.float64, device=DEV)
+    nbr, nbr_shift, nnei = nga.nl_build(pos, (5.0, 5.0, 5.0), 2.0, 4)
+    csr = nga.edge_csr(nbr, nbr_shift, nnei)
+    assert csr["n_edges"] == 0 and csr["row_ptr"].cpu().tolist() == [0]
+    g = _gpu_csr(np.array([[1.0, 2.0, 3.0]]), (10.0, 10.0, 10.0), 2.0, 4)
+    assert g["row_ptr"].tolist() == [0, 0] and g["nbr"].tolist() == [[-1, -1, -1, -1]]
+
+
+def test_deterministic():
+    w = W.WORKLOADS[3]
+    pos, box = W.workload_positions(w)
+    a = _gpu_csr(pos, box, w.rcut, w.sel)
+    b = _gpu_csr(pos, box, w.rcut, w.sel)
+    for k in ("row_ptr", "col", "shift", "edge_vec", "nbr", "nbr_shift"):
+        assert np.array_equal(a[k], b[k])
+
+
+def test_edge_mask_compaction_keeps_slot_order():
+    """An external padded list with holes (-1) compacts in slot order (the edge mask)."""
+    rng = np.random.default_rng(3)
+    n, sel = 50, 37
+    nbr = rng.integers(0, n, size=(n, sel)).astype(np.int32)
+    nbr[rng.random((n, sel)) < 0.4] = -1
+    nbr[7] = -1
+    sh = rng.integers(-2, 3, size=(n, sel, 3)).astype(np.int32)
+    csr = nga.edge_csr(torch.from_numpy(nbr).to(DEV), torch.from_numpy(sh).to(DEV), None)
+    nga.check_status(csr["ws"], "mask csr")
+    mask = nbr >= 0
+    assert np.array_equal(csr["row_ptr"].cpu().numpy(), np.concatenate([[0], np.cumsum(mask.sum(1))]))
+    assert np.array_equal(csr["col"].cpu().numpy(), nbr[mask])
+    assert np.array_equal(csr["shift"].cpu().numpy(), sh[mask])
+    assert np.array_equal(csr["dst"].cpu().numpy(), np.nonzero(mask)[0])
+
+
+def _expect_status(ws, code):
+    assert nga.sync_status(ws) == code
+    assert nga.sync_status(ws) == 0  # cleared by the read
+
+
+@pytest.mark.parametrize("bad", [10.0, -1e-300, float("nan"), float("inf")])
+def test_position_outside_box_is_reported(bad):
+    pos = torch.tensor([[1.0, 1.0, 1.0], [2.0, bad, 3.0]], dtype=torch.float64, device=DEV)
+    ws = nga.Workspace(DEV)
+    nga.nl_build(pos, (10.0, 10.0, 10.0), 3.0, 4, ws=ws)
+    _expect_status(ws, -2)
+
+
+def test_row_capacity_is_reported():
+    pos = W.random_positions(700, (3.0, 3.0, 3.0), 11) * 0.5 + 1.0  # 700 atoms inside 1.5 A
+    ws = nga.Workspace(DEV)
+    nga.nl_build(torch.from_numpy(pos).to(DEV), (20.0, 20.0, 20.0), 2.7, 16, ws=ws)
+    _expect_status(ws, -3)
+
+
+def test_edge_capacity_and_bad_index_are_reported():
+    w = W.WORKLOADS[1]
+    pos, box = W.workload_positions(w)
+    p = torch.from_numpy(pos).to(DEV)
+    nbr, nbr_shift, nnei = nga.nl_build(p, box, w.rcut, w.sel)
+    with pytest.raises(nga.NGAError) as ex:
+        nga.edge_csr(nbr, nbr_shift, nnei, e_cap=100)
+    assert ex.value.code == -4
+    nbr[3, 5] = 10 ** 6
+    with pytest.raises(nga.NGAError) as ex:
+        nga.edge_csr(nbr, nbr_shift, nnei)
+    assert ex.value.code == -8
