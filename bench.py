@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Throughput of the neighbour-graph attention hot path on one MI355X.
+
+One step = nl_build (cell-list neighbour rows) + edge_csr (destination CSR) +
+block_attn_forward (all attention layers), every input resident in HBM, all
+on torch's current stream, no host synchronisation inside the step.  The
+workload defaults to Fe BCC, 32^3 cubic cells (65,536 atoms), rcut 8 A,
+sel 181, 64 fp32 channels, 4 heads, 1 layer: the system size at which the
+deepmd-kit DPA4 issue quotes atom-step/s.  Atoms/s = N / step time.
+
+Prints one JSON line with the value, a roofline entry for the dominant
+kernel (live HIP-event timing of its launches) and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "atoms/s for NL build + block-dense neighbour attention fwd; % of roofline"
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}   # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0                        # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4, help="workload key (1..5), default 4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(reference kernel for HBM counter scaling)")
+    return ap.parse_args()
+
+
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def attention_sources(variant: str):
+    base = "neighbour_graph_attention_amd/csrc/"
+    if variant.startswith("fused"):
+        return [base + "block_attn_fused.hip", base + "block_attn_fused.h"]
+    return [base + "block_attn.hip"]
+
+
+def load_traffic(variant: str, workload: str):
+    """Measured HBM bytes per launch of the attention kernel, if the committed counter summary
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{variant}.{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    if doc.get("source_sha256") != source_digest(attention_sources(variant)):
+        return None
+    return float(doc["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(w, pos, box, rp, x, wt, target_s):
+    """The oracle (brute-force rows + naive attention through every layer) on sampled centres."""
+    import oracle
+
+    n = pos.shape[0]
+    rng = np.random.default_rng(4242)
+
+    def run(m):
+        centres = np.sort(rng.choice(n, m, replace=False))
+        t0 = time.perf_counter()
+        srp, scol, sshift, svec = oracle.nl_rows(pos, box, w.rcut, w.sel, centres)
+        xs = np.concatenate([x[rp[i]:rp[i + 1]] for i in centres]).astype(np.float64)
+        oracle.attn_naive(srp, xs, wt.astype(np.float64), w.heads)
+        return time.perf_counter() - t0
+
+    m0 = min(n, 32)
+    t0 = run(m0)
+    m = int(min(n, max(m0, m0 * target_s / max(t0, 1e-6))))
+    t = run(m)
+    return {"value": m / t, "unit": "atoms/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{m} random centres of {n}: brute-force rows over all atoms and images, "
+                      f"then naive attention through {w.layers} layer(s); {t:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import neighbour_graph_attention_amd as nga
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    pos_np, box = W.workload_positions(w)
+    n = pos_np.shape[0]
+    pos = torch.from_numpy(pos_np).to(dev)
+
+    # Buffers and workspaces, allocated once.
+    nbr = torch.empty((n, w.sel), dtype=torch.int32, device=dev)
+    nbr_shift = torch.empty((n, w.sel, 3), dtype=torch.int32, device=dev)
+    nnei = torch.empty((n,), dtype=torch.int32, device=dev)
+    e_cap = n * w.sel
+    csr_out = {
+        "row_ptr": torch.empty((n + 1,), dtype=torch.int64, device=dev),
+        "col": torch.empty((e_cap,), dtype=torch.int32, device=dev),
+        "shift": torch.empty((e_cap, 3), dtype=torch.int32, device=dev),
+        "dst": torch.empty((e_cap,), dtype=torch.int32, device=dev),
+    }
+    ws_nl = nga.Workspace(dev, nga.nl_build_workspace_bytes(n, box, w.rcut))
+    ws_csr = nga.Workspace(dev)
+
+    # One untimed pass reads E back (the only host synchronisation of the run).
+    nga.nl_build(pos, box, w.rcut, w.sel, nbr=nbr, nbr_shift=nbr_shift, nnei=nnei, ws=ws_nl)
+    first = nga.edge_csr(nbr, nbr_shift, nnei, out=csr_out, ws=ws_csr)
+    nga.check_status(ws_nl, "nl_build")
+    e = first["n_edges"]
+    rp = csr_out["row_ptr"].cpu().numpy()
+
+    x_np = W.workload_features(w, e)
+    wt_np = W.workload_weights(w)
+    x = torch.from_numpy(x_np).to(dev)
+    wt = torch.from_numpy(wt_np).to(dev)
+    y = torch.empty_like(x)
+    dtype_code = nga.NGA_F64 if w.dtype == "f64" else nga.NGA_F32
+    variant = nga.attn_variant(dtype_code, w.sel, w.c, w.heads)
+    ws_attn = nga.Workspace(dev, nga.block_attn_workspace_bytes(dtype_code, e, w.sel, w.c,
+                                                                w.heads, w.layers))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        nga.nl_build(pos, box, w.rcut, w.sel, nbr=nbr, nbr_shift=nbr_shift, nnei=nnei, ws=ws_nl)
+        if ev is not None:
+            ev[1].record(stream)
+        nga.edge_csr(nbr, nbr_shift, nnei, e_cap=e_cap, read_n_edges=False, out=csr_out,
+                     ws=ws_csr)
+        if ev is not None:
+            ev[2].record(stream)
+        nga.block_attn_forward(csr_out["row_ptr"], x, wt, w.heads, w.sel, y=y, ws=ws_attn)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    for ws, name in ((ws_nl, "nl_build"), (ws_csr, "edge_csr"), (ws_attn, "block_attn_forward")):
+        nga.check_status(ws, name)
+    if not bool(torch.isfinite(y).all()):
+        raise RuntimeError("non-finite attention output")
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    part = np.array([[ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
+                      ev[2].elapsed_time(ev[3])] for ev in events])
+    nl_ms, csr_ms, attn_ms = (float(v) for v in part.mean(axis=0))
+
+    if args.copy_calib_mib > 0:
+        nel = args.copy_calib_mib * (1 << 20) // 4
+        src = torch.ones(nel, dtype=torch.float32, device=dev)
+        dstb = torch.empty_like(src)
+        dstb.copy_(src)
+        torch.cuda.synchronize(dev)
+
+    counts = np.diff(rp).astype(np.float64)
+    flops = w.layers * float(np.sum(8.0 * w.c * w.c * counts + 4.0 * w.c * counts * counts))
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = load_traffic(variant, w.name)
+    nl_bytes = 24.0 * n + 8.0 * (n + 1) + 16.0 * e
+    nl_gbs = nl_bytes / ((nl_ms + csr_ms) * 1e-3) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": n / (ms_step * 1e-3),
+        "unit": "atoms/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_atoms": n, "n_edges": e, "rcut": w.rcut, "sel": w.sel,
+                   "channels": w.c, "heads": w.heads, "layers": w.layers,
+                   "geometry_dtype": "f64", "attn_kernel": variant},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic,
+                     "kernel": variant, "flops_per_launch": flops, "launch_ms": attn_ms},
+        "parts_ms": {"nl_build": nl_ms, "edge_csr": csr_ms, "block_attn_forward": attn_ms},
+        "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
+                   "frac": nl_gbs / PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, pos_np, box, rp, x_np, wt_np, args.cpu_seconds)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

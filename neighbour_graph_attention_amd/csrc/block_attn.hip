@@ -299,7 +299,11 @@ extern "C" size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t
                                              int32_t c, int32_t n_heads, int32_t n_layers) {
     if (dtype != NGA_F64 && dtype != NGA_F32) return 0;
     if (n_edges < 0 || c < 1 || n_heads < 1 || n_layers < 1 || nnei_cap < 1) return 0;
-    if (nga::use_fused(dtype, nnei_cap, c, n_heads)) return nga::align_up(sizeof(nga::WsHeader));
+    if (nga::use_fused(dtype, nnei_cap, c, n_heads)) {
+        nga::Carver cv(nullptr);
+        cv.take<float>(nga::fused_workspace_floats(c, n_layers));
+        return cv.off;
+    }
     const size_t es = dtype == NGA_F64 ? sizeof(double) : sizeof(float);
     return nga::carve_generic(nullptr, n_edges, c, n_layers, es).bytes;
 }
@@ -335,13 +339,16 @@ extern "C" int block_attn_forward(int dtype, const int64_t* row_ptr, const int32
     if (n_centres == 0 || n_edges == 0) return NGA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t* status = &static_cast<WsHeader*>(ws)->status;
+    if (use_fused(dtype, nnei_cap, c, n_heads)) {  // the fused kernel checks row_ptr itself
+        Carver cv(ws);
+        float* packed = cv.take<float>(fused_workspace_floats(c, n_layers));
+        return run_fused(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
+                         weights, x, y, packed, status, s);
+    }
     hipLaunchKernelGGL(check_rows_kernel, dim3(1), dim3(1), 0, s, row_ptr, (int)n_centres, n_edges,
                        status);
     int rc = last_launch_status();
     if (rc) return rc;
-    if (use_fused(dtype, nnei_cap, c, n_heads))
-        return run_fused(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
-                         weights, x, y, status, s);
     if (dtype == NGA_F64)
         return run_generic<double>(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads,
                                    n_layers, static_cast<const double*>(weights),

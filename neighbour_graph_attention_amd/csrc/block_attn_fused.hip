@@ -1,15 +1,305 @@
-// Fused per-centre attention kernels.
+// Fused per-centre block attention, fp32, 16-wide heads, on CDNA matrix cores.
+//
+// deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than dense ...", section
+// "Proposed fix: block-dense attention on the graph": gather a centre's (nnei, c) block
+// through the destination CSR, dense attention math with a mask for the ragged tail,
+// scatter back to the edge axis.  Here the whole layer stack of one centre runs in one
+// work-group and nothing but the input and output rows touches HBM.
+//
+// Work-group = H wavefronts, wavefront h owns head h (columns 16h .. 16h+15).  All
+// contractions are v_mfma_f32_16x16x4_f32.  Its operand / result layouts (A[i][k] from lane
+// i + 16k, B[k][j] from lane j + 16k, D[i][j] in lane j + 16*(i/4), register i%4) let every
+// result feed the next contraction directly, by choosing the order in which each
+// contraction walks its k index:
+//   projections  Q^T = Wq_h^T X^T, K^T = Wk_h^T X^T, V = X Wv_h   (k = input channel)
+//                with k(step kk, lane group g) = 16*(kk/4) + 4g + kk%4, so a lane loads
+//                four float4 of its own row;
+//   scores       S^T = K Q^T, k = head channel 4g + r: A = K^T result register r,
+//                B = Q^T result register r;  lane (g, i) then holds query i against keys
+//                4g+r of every key tile;
+//   softmax      row max / sum over a lane's registers and the 4 lane groups (2 shuffles);
+//   values       O^T = V^T P^T, k = key 16kt + 4g + r: A = V result register r,
+//                B = P register r;
+//   output       Y^T = Wo^T [O_0 .. O_{H-1}]^T, k = 16hh + 4g + r: B = head hh's O^T
+//                register r, exchanged through LDS; lane (g, i) gets 4 consecutive output
+//                channels of row i, stored as one float4.
+// Rows past the centre's length are loaded as zeros, their keys masked to -inf, their
+// outputs never stored.  Stacked layers run in place on y: every row of a centre is read
+// (Q to LDS, K and V to registers) before any of its rows is written.
 #include "block_attn_fused.h"
 
 namespace nga {
 
-bool fused_supported(int, int32_t, int32_t, int32_t) { return false; }
+namespace {
 
-const char* fused_name(int, int32_t, int32_t) { return "none"; }
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-int run_fused(int, const int64_t*, const int32_t*, int64_t, int64_t, int32_t, int32_t, int32_t,
-              int32_t, const void*, const void*, void*, uint32_t*, hipStream_t) {
-    return NGA_EINVAL;
+__device__ inline f4 mfma4(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Weights in operand order: for layer l, matrix m (q, k, v, o) and wavefront h, lane L holds
+// KS consecutive floats, element kk = W_m[k(kk, g)][16h + i] (lane L = 16g + i).
+__global__ void pack_weights_kernel(const float* __restrict__ w, int C, int H, int layers,
+                                    float* __restrict__ packed) {
+    const int KS = C / 4;
+    const int64_t total = (int64_t)layers * 4 * C * C;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        int64_t rest = idx;
+        const int kk = (int)(rest % KS); rest /= KS;
+        const int lane = (int)(rest % 64); rest /= 64;
+        const int h = (int)(rest % H); rest /= H;
+        const int m = (int)(rest % 4); rest /= 4;
+        const int l = (int)rest;
+        const int g = lane >> 4, i = lane & 15;
+        const int k = 16 * (kk >> 2) + 4 * g + (kk & 3);
+        packed[idx] = w[(((int64_t)l * 4 + m) * C + k) * C + 16 * h + i];
+    }
+}
+
+struct FusedArgs {
+    const int64_t* row_ptr;
+    const int32_t* order;
+    const float* x;
+    float* y;
+    const float* w;  // packed operand-order weights
+    int n_centres;
+    int64_t n_edges;
+    int nnei_cap;
+    int layers;
+    uint32_t* status;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One layer of one centre whose row has n edges, NT = ceil(n / 16) tiles.
+template <int H, int NT>
+__device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __restrict__ src,
+                                             const float* __restrict__ P, int64_t r0, int n,
+                                             f4 (*__restrict__ sQh)[64], f4 (*__restrict__ sO)[H][64],
+                                             float (*__restrict__ sWoh)[64], int lane, int h,
+                                             bool& bad_index) {
+    constexpr int C = 16 * H;
+    constexpr int KS = C / 4;
+    constexpr int MAT = H * 64 * KS;
+    const int g = lane >> 4;
+    const int li = lane & 15;
+    const float c1 = kLog2e * 0.25f;  // log2(e) / sqrt(16)
+
+    float wq[KS], wk[KS], wv[KS];
+#pragma unroll
+    for (int k4 = 0; k4 < KS / 4; ++k4) {
+        const f4 a = *reinterpret_cast<const f4*>(P + 0 * MAT + 4 * k4);
+        const f4 b = *reinterpret_cast<const f4*>(P + 1 * MAT + 4 * k4);
+        const f4 c = *reinterpret_cast<const f4*>(P + 2 * MAT + 4 * k4);
+        const f4 d = *reinterpret_cast<const f4*>(P + 3 * MAT + 4 * k4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            wq[4 * k4 + i] = a[i];
+            wk[4 * k4 + i] = b[i];
+            wv[4 * k4 + i] = c[i];
+            sWoh[4 * k4 + i][lane] = d[i];
+        }
+    }
+
+    // Phase 1: Q^T to LDS, K^T and V in registers, one row tile at a time.
+    f4 kt[NT], vt[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int a = 16 * t + li;
+        int64_t row = -1;
+        if (a < n) {
+            row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+            if (row < 0 || row >= A.n_edges) { bad_index = true; row = -1; }
+        }
+        float xo[KS];
+#pragma unroll
+        for (int u = 0; u < C / 16; ++u) {
+            f4 v = {0.f, 0.f, 0.f, 0.f};
+            if (row >= 0) v = *reinterpret_cast<const f4*>(src + row * C + 16 * u + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xo[4 * u + i] = v[i];
+        }
+        f4 q = {0.f, 0.f, 0.f, 0.f}, k = q, v = q;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            q = mfma4(wq[kk], xo[kk], q);
+            k = mfma4(wk[kk], xo[kk], k);
+            v = mfma4(xo[kk], wv[kk], v);
+        }
+        sQh[t][lane] = q;
+        kt[t] = k;
+        vt[t] = v;
+        __builtin_amdgcn_sched_barrier(0);  // one tile's loads in flight at a time
+    }
+
+    // Phases 2 + 3, one query tile at a time.
+    for (int qt = 0; qt < NT; ++qt) {
+        const f4 q = sQh[qt][lane];
+        f4 s[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc = mfma4(kt[t][r], q[r], acc);
+            s[t] = acc;
+        }
+        // Only the last key tile can hold keys past the row end.
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            if (16 * (NT - 1) + 4 * g + r >= n) s[NT - 1][r] = -INFINITY;
+        float m = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m = fmaxf(m, s[t][r]);
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const float mc = m * c1;
+        float z = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(s[t][r] * c1 - mc);
+                s[t][r] = p;
+                z += p;
+            }
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        f4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (t & 1) o1 = mfma4(vt[t][r], s[t][r], o1);
+                else o0 = mfma4(vt[t][r], s[t][r], o0);
+            }
+        }
+        const f4 o = (o0 + o1) * (1.0f / z);
+
+        const int buf = qt & 1;
+        sO[buf][h][lane] = o;
+        __syncthreads();
+        f4 ya[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ya[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh) {
+            const f4 oo = sO[buf][hh][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ya[hh & 3] = mfma4(sWoh[4 * hh + r][lane], oo[r], ya[hh & 3]);
+        }
+        const f4 yv = (ya[0] + ya[1]) + (ya[2] + ya[3]);
+        const int a = 16 * qt + li;
+        if (a < n) {
+            const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+            if (row >= 0 && row < A.n_edges)
+                *reinterpret_cast<f4*>(A.y + row * C + 16 * h + 4 * g) = yv;
+        }
+    }
+}
+
+template <int H, int TMAX>
+__global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
+    constexpr int C = 16 * H;
+    constexpr int KS = C / 4;
+    __shared__ f4 sQ[H][TMAX][64];
+    __shared__ f4 sO[2][H][64];
+    __shared__ float sWo[H][KS][64];
+
+    const int lane = threadIdx.x & 63;
+    const int h = threadIdx.x >> 6;
+
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (A.row_ptr[0] != 0 || A.row_ptr[A.n_centres] > A.n_edges) raise_bits(A.status, kBitCap);
+    }
+    bool bad_index = false;
+    for (int centre = blockIdx.x; centre < A.n_centres; centre += gridDim.x) {
+        const int64_t r0 = A.row_ptr[centre];
+        const int64_t r1 = A.row_ptr[centre + 1];
+        const int n = (int)(r1 - r0);
+        if (n <= 0) continue;
+        if (n > A.nnei_cap || n > 16 * TMAX || r0 < 0 || r1 > A.n_edges) {
+            if (threadIdx.x == 0) raise_bits(A.status, kBitCap);
+            continue;
+        }
+        const int nt = (n + 15) >> 4;
+        for (int layer = 0; layer < A.layers; ++layer) {
+            const float* src = layer == 0 ? A.x : A.y;
+            const float* P = A.w + (size_t)layer * 4 * C * C + ((size_t)h * 64 + lane) * KS;
+#define NGA_CASE(T)                                                                          \
+    case T:                                                                                  \
+        if constexpr (T <= TMAX)                                                             \
+            centre_layer<H, T>(A, src, P, r0, n, sQ[h], sO, sWo[h], lane, h, bad_index);     \
+        break;
+            switch (nt) {
+                NGA_CASE(1) NGA_CASE(2) NGA_CASE(3) NGA_CASE(4) NGA_CASE(5) NGA_CASE(6)
+                NGA_CASE(7) NGA_CASE(8) NGA_CASE(9) NGA_CASE(10) NGA_CASE(11) NGA_CASE(12)
+                default: break;
+            }
+#undef NGA_CASE
+            __syncthreads();  // this layer's rows are stored before the next layer reads them
+        }
+    }
+    if (bad_index) raise_bits(A.status, kBitIndex);
+}
+
+template <int H>
+int launch_h(int tmax, const FusedArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_centres), block(64 * H);
+    if (tmax <= 4) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 4>), grid, block, 0, s, a);
+    else if (tmax <= 8) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 8>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fused_f32_d16_kernel<H, 12>), grid, block, 0, s, a);
+    return last_launch_status();
+}
+
+}  // namespace
+
+bool fused_supported(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
+    if (dtype != NGA_F32) return false;
+    if (heads < 1 || c != 16 * heads) return false;
+    if (heads != 1 && heads != 2 && heads != 4) return false;
+    return nnei_cap >= 1 && nnei_cap <= 16 * 12;
+}
+
+const char* fused_name(int dtype, int32_t c, int32_t heads) {
+    (void)dtype; (void)c; (void)heads;
+    return "fused_f32_d16";
+}
+
+size_t fused_workspace_floats(int32_t c, int32_t layers) { return (size_t)layers * 4 * c * c; }
+
+int run_fused(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+              int64_t n_edges, int32_t nnei_cap, int32_t c, int32_t heads, int32_t layers,
+              const void* weights, const void* x, void* y, void* packed, uint32_t* status,
+              hipStream_t s) {
+    (void)dtype;
+    const int64_t total = (int64_t)layers * 4 * c * c;
+    const unsigned pblocks = (unsigned)std::min<int64_t>((total + 255) / 256, 1024);
+    hipLaunchKernelGGL(pack_weights_kernel, dim3(pblocks), dim3(256), 0, s,
+                       static_cast<const float*>(weights), (int)c, (int)heads, (int)layers,
+                       static_cast<float*>(packed));
+    int rc = last_launch_status();
+    if (rc) return rc;
+    FusedArgs a;
+    a.row_ptr = row_ptr;
+    a.order = order;
+    a.x = static_cast<const float*>(x);
+    a.y = static_cast<float*>(y);
+    a.w = static_cast<const float*>(packed);
+    a.n_centres = (int)n_centres;
+    a.n_edges = n_edges;
+    a.nnei_cap = nnei_cap;
+    a.layers = layers;
+    a.status = status;
+    const int tmax = (nnei_cap + 15) / 16;
+    switch (heads) {
+        case 1: return launch_h<1>(tmax, a, s);
+        case 2: return launch_h<2>(tmax, a, s);
+        default: return launch_h<4>(tmax, a, s);
+    }
 }
 
 }  // namespace nga

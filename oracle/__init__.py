@@ -51,6 +51,8 @@ def _load():
     i64, i32, dbl, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p
     lib.orc_nl_row.restype = i64
     lib.orc_nl_row.argtypes = [vp, i64, vp, dbl, i32, i64, vp, vp, vp, vp, vp]
+    lib.orc_nl_rows.restype = ctypes.c_int
+    lib.orc_nl_rows.argtypes = [vp, i64, vp, dbl, i32, vp, i64, vp, vp, vp, vp]
     lib.orc_nl_full.restype = i64
     lib.orc_nl_full.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, vp, i64]
     for name in ("orc_attn_naive", "orc_attn_pairaxis"):
@@ -93,6 +95,27 @@ def nl_row(pos, box, rcut: float, sel: int, i: int):
     if k < 0:
         raise MemoryError("oracle nl_row failed")
     return col[:k].copy(), shift[:k].copy(), vec[:k].copy(), r2[:k].copy(), int(nw.value)
+
+
+def nl_rows(pos, box, rcut: float, sel: int, centres):
+    """Rows of the listed centres as a CSR over the list: (row_ptr, col, shift, vec)."""
+    lib = _load()
+    pos = _f64(pos)
+    box = _f64(box)
+    centres = np.ascontiguousarray(centres, dtype=np.int64)
+    m = centres.shape[0]
+    counts = np.empty(m, np.int64)
+    col = np.empty((max(m, 1), sel), np.int32)
+    shift = np.empty((max(m, 1), sel, 3), np.int32)
+    vec = np.empty((max(m, 1), sel, 3), np.float64)
+    rc = lib.orc_nl_rows(_ptr(pos), pos.shape[0], _ptr(box), float(rcut), int(sel), _ptr(centres),
+                         m, _ptr(counts), _ptr(col), _ptr(shift), _ptr(vec))
+    if rc != 0:
+        raise MemoryError("oracle nl_rows failed")
+    row_ptr = np.zeros(m + 1, np.int64)
+    np.cumsum(counts, out=row_ptr[1:])
+    keep = np.arange(sel)[None, :] < counts[:, None]
+    return row_ptr, col[:m][keep], shift[:m][keep], vec[:m][keep]
 
 
 def nl_full(pos, box, rcut: float, sel: int):

@@ -138,6 +138,27 @@ int64_t orc_nl_row(const double* pos, int64_t n_atoms, const double* box, double
 }
 
 /*
+ * Rows of a list of centres (OpenMP over the list): counts[n_list], and for
+ * list entry t its row in col[t*sel ..], shift[(t*sel)*3 ..], vec (nullable).
+ * Returns 0, or -1 if memory runs out.
+ */
+int orc_nl_rows(const double* pos, int64_t n_atoms, const double* box, double rcut, int32_t sel,
+                const int64_t* centres, int64_t n_list, int64_t* counts, int32_t* col,
+                int32_t* shift, double* vec)
+{
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t t = 0; t < n_list; ++t) {
+        int64_t k = orc_nl_row(pos, n_atoms, box, rcut, sel, centres[t], col + (size_t)t * sel,
+                               shift + (size_t)t * sel * 3, vec ? vec + (size_t)t * sel * 3 : NULL,
+                               NULL, NULL);
+        if (k < 0) failed = 1;
+        counts[t] = k < 0 ? 0 : k;
+    }
+    return failed ? -1 : 0;
+}
+
+/*
  * Whole destination CSR for all centres: row_ptr[n_atoms+1], col[e_cap],
  * shift[e_cap][3], vec[e_cap][3] (nullable).  Returns E, or -1 if E would
  * exceed e_cap or memory runs out.  Rows are built independently (OpenMP

@@ -139,39 +139,48 @@ def test_deterministic_and_cap_independent(dtype, c, heads, cap):
     a = _run(rp, x, wt, heads, cap)
     b = _run(rp, x, wt, heads, cap)
     assert np.array_equal(a, b)
-    c2 = _run(rp, x, wt, heads, cap + 37)  # more masked padding changes nothing
+    bigger = cap + 10  # a larger cap within the same kernel variant changes nothing
+    dt = 0 if dtype == np.float64 else 1
+    assert nga.attn_variant(dt, bigger, c, heads) == nga.attn_variant(dt, cap, c, heads)
+    c2 = _run(rp, x, wt, heads, bigger)
     assert np.array_equal(a, c2)
 
 
-def test_rows_untouched_outside_centres():
+PATH_CASES = [(np.float64, 4), (np.float32, 1)]  # generic path, fused path
+
+
+@pytest.mark.parametrize("dtype,heads", PATH_CASES)
+def test_rows_untouched_outside_centres(dtype, heads):
     rp = np.array([0, 3, 3, 7], np.int64)
-    x = W.make_features(10, 16, 1)
-    wt = W.make_weights(1, 16, 2)
+    x = W.make_features(10, 16, 1, dtype)
+    wt = W.make_weights(1, 16, 2, dtype)
     xt = torch.from_numpy(x).to(DEV)
     y = torch.full_like(xt, 7.0)
     ws = nga.Workspace(DEV)
-    nga.block_attn_forward(torch.from_numpy(rp).to(DEV), xt, torch.from_numpy(wt).to(DEV), 4, 8,
-                           y=y, ws=ws)
+    nga.block_attn_forward(torch.from_numpy(rp).to(DEV), xt, torch.from_numpy(wt).to(DEV), heads,
+                           8, y=y, ws=ws)
     nga.check_status(ws)
     assert torch.all(y[7:] == 7.0)
 
 
-def test_row_over_cap_is_reported():
+@pytest.mark.parametrize("dtype,heads", PATH_CASES)
+def test_row_over_cap_is_reported(dtype, heads):
     rp = np.array([0, 5, 30], np.int64)
-    x = W.make_features(30, 16, 1)
-    wt = W.make_weights(1, 16, 2)
+    x = W.make_features(30, 16, 1, dtype)
+    wt = W.make_weights(1, 16, 2, dtype)
     ws = nga.Workspace(DEV)
     nga.block_attn_forward(torch.from_numpy(rp).to(DEV), torch.from_numpy(x).to(DEV),
-                           torch.from_numpy(wt).to(DEV), 4, 10, ws=ws)
+                           torch.from_numpy(wt).to(DEV), heads, 10, ws=ws)
     assert nga.sync_status(ws) == -4
 
 
-def test_order_out_of_range_is_reported():
+@pytest.mark.parametrize("dtype,heads", PATH_CASES)
+def test_order_out_of_range_is_reported(dtype, heads):
     rp = np.array([0, 4, 8], np.int64)
-    x = W.make_features(8, 16, 1)
-    wt = W.make_weights(1, 16, 2)
+    x = W.make_features(8, 16, 1, dtype)
+    wt = W.make_weights(1, 16, 2, dtype)
     order = torch.tensor([0, 1, 2, 3, 4, 5, 6, 99], dtype=torch.int32, device=DEV)
     ws = nga.Workspace(DEV)
     nga.block_attn_forward(torch.from_numpy(rp).to(DEV), torch.from_numpy(x).to(DEV),
-                           torch.from_numpy(wt).to(DEV), 4, 8, order=order, ws=ws)
+                           torch.from_numpy(wt).to(DEV), heads, 8, order=order, ws=ws)
     assert nga.sync_status(ws) == -8
