@@ -88,7 +88,7 @@ def cpu_baseline(w, pos, box, rp, x, wt, target_s):
         oracle.attn_naive(srp, xs, wt.astype(np.float64), w.heads)
         return time.perf_counter() - t0
 
-    m0 = min(n, 32)
+    m0 = min(n, 256)
     t0 = run(m0)
     m = int(min(n, max(m0, m0 * target_s / max(t0, 1e-6))))
     t = run(m)

@@ -3,8 +3,9 @@
 // deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than dense ...", section
 // "Proposed fix: block-dense attention on the graph": gather a centre's (nnei, c) block
 // through the destination CSR, dense attention math with a mask for the ragged tail,
-// scatter back to the edge axis.  Here the whole layer stack of one centre runs in one
-// work-group and nothing but the input and output rows touches HBM.
+// scatter back to the edge axis.  Here one work-group runs a centre's whole layer stack:
+// the block is gathered once into LDS, intermediate layers hand their output back through
+// the same LDS rows, and only the last layer writes to HBM.
 //
 // Work-group = H wavefronts, wavefront h owns head h (columns 16h .. 16h+15).  All
 // contractions are v_mfma_f32_16x16x4_f32.  Its operand / result layouts (A[i][k] from lane
@@ -12,8 +13,8 @@
 // result feed the next contraction directly, by choosing the order in which each
 // contraction walks its k index:
 //   projections  Q^T = Wq_h^T X^T, K^T = Wk_h^T X^T, V = X Wv_h   (k = input channel)
-//                with k(step kk, lane group g) = 16*(kk/4) + 4g + kk%4, so a lane loads
-//                four float4 of its own row;
+//                with k(step kk, lane group g) = 16*(kk/4) + 4g + kk%4, so a lane reads
+//                four float4 of its own row of the block;
 //   scores       S^T = K Q^T, k = head channel 4g + r: A = K^T result register r,
 //                B = Q^T result register r;  lane (g, i) then holds query i against keys
 //                4g+r of every key tile;
@@ -22,10 +23,15 @@
 //                B = P register r;
 //   output       Y^T = Wo^T [O_0 .. O_{H-1}]^T, k = 16hh + 4g + r: B = head hh's O^T
 //                register r, exchanged through LDS; lane (g, i) gets 4 consecutive output
-//                channels of row i, stored as one float4.
-// Rows past the centre's length are loaded as zeros, their keys masked to -inf, their
-// outputs never stored.  Stacked layers run in place on y: every row of a centre is read
-// (Q to LDS, K and V to registers) before any of its rows is written.
+//                channels of row i, one float4.
+// K^T and V of every row tile stay in registers for the whole layer; Q^T is formed one
+// query tile at a time.  Rows past the centre's length are zeros in LDS, their keys are
+// masked to -inf and their outputs are never stored.
+//
+// On gfx950 the fp32 MFMA and the VALU do not execute concurrently (the co-execution counter
+// stays at zero and MFMA-busy + VALU-busy add up to the kernel time), so the softmax's VALU
+// instructions add directly to the MFMA time: every contraction accumulates in a single
+// chain (no partial sums to add up) and 1/Z uses the hardware reciprocal.
 #include "block_attn_fused.h"
 
 namespace nga {
@@ -73,13 +79,26 @@ struct FusedArgs {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One layer of one centre whose row has n edges, NT = ceil(n / 16) tiles.
+// Row stride (floats) of the LDS block: 4 floats of padding per row spread the float4 reads
+// of the 16 rows of a tile over the LDS banks.
+template <int H>
+struct Lds {
+    static constexpr int C = 16 * H;
+    static constexpr int XS = C + 4;
+};
+
+// One layer of one centre whose block (NT row tiles) sits in sX.  K^T and V of every tile go
+// to registers; then for each query tile, Q^T is formed from the block, the scores, softmax
+// and values follow, the heads' outputs meet in LDS for the output projection, and the
+// result is stored to y (last layer) or written back over the block rows it came from
+// (earlier layers; those rows are no longer read in this layer).
 template <int H, int NT>
-__device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __restrict__ src,
-                                             const float* __restrict__ P, int64_t r0, int n,
-                                             f4 (*__restrict__ sQh)[64], f4 (*__restrict__ sO)[H][64],
-                                             float (*__restrict__ sWoh)[64], int lane, int h,
-                                             bool& bad_index) {
+__device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __restrict__ P,
+                                             const int64_t r0, const int n, const bool last,
+                                             float (*__restrict__ sX)[Lds<H>::XS],
+                                             f4 (*__restrict__ sO)[H][64],
+                                             float (*__restrict__ sWoh)[64], const int lane,
+                                             const int h) {
     constexpr int C = 16 * H;
     constexpr int KS = C / 4;
     constexpr int MAT = H * 64 * KS;
@@ -103,40 +122,41 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __
         }
     }
 
-    // Phase 1: Q^T to LDS, K^T and V in registers, one row tile at a time.
+    // Phase 1: K^T and V of every row tile, kept in registers.
     f4 kt[NT], vt[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int a = 16 * t + li;
-        int64_t row = -1;
-        if (a < n) {
-            row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
-            if (row < 0 || row >= A.n_edges) { bad_index = true; row = -1; }
-        }
         float xo[KS];
 #pragma unroll
         for (int u = 0; u < C / 16; ++u) {
-            f4 v = {0.f, 0.f, 0.f, 0.f};
-            if (row >= 0) v = *reinterpret_cast<const f4*>(src + row * C + 16 * u + 4 * g);
+            const f4 v = *reinterpret_cast<const f4*>(&sX[16 * t + li][16 * u + 4 * g]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) xo[4 * u + i] = v[i];
         }
-        f4 q = {0.f, 0.f, 0.f, 0.f}, k = q, v = q;
+        f4 k = {0.f, 0.f, 0.f, 0.f}, v = k;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            q = mfma4(wq[kk], xo[kk], q);
             k = mfma4(wk[kk], xo[kk], k);
             v = mfma4(xo[kk], wv[kk], v);
         }
-        sQh[t][lane] = q;
         kt[t] = k;
         vt[t] = v;
-        __builtin_amdgcn_sched_barrier(0);  // one tile's loads in flight at a time
     }
 
     // Phases 2 + 3, one query tile at a time.
     for (int qt = 0; qt < NT; ++qt) {
-        const f4 q = sQh[qt][lane];
+        f4 q = {0.f, 0.f, 0.f, 0.f};
+        {
+            float xo[KS];
+#pragma unroll
+            for (int u = 0; u < C / 16; ++u) {
+                const f4 v = *reinterpret_cast<const f4*>(&sX[16 * qt + li][16 * u + 4 * g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xo[4 * u + i] = v[i];
+            }
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) q = mfma4(wq[kk], xo[kk], q);
+        }
         f4 s[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -168,35 +188,33 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __
             }
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
-        f4 o0 = {0.f, 0.f, 0.f, 0.f}, o1 = o0;
+        f4 osum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (t & 1) o1 = mfma4(vt[t][r], s[t][r], o1);
-                else o0 = mfma4(vt[t][r], s[t][r], o0);
-            }
-        }
-        const f4 o = (o0 + o1) * (1.0f / z);
+            for (int r = 0; r < 4; ++r) osum = mfma4(vt[t][r], s[t][r], osum);
+        const f4 o = osum * __builtin_amdgcn_rcpf(z);
 
         const int buf = qt & 1;
         sO[buf][h][lane] = o;
-        __syncthreads();
-        f4 ya[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ya[j] = f4{0.f, 0.f, 0.f, 0.f};
+        __syncthreads();  // every head's O of this tile is in LDS; every wave has read rows qt
+        f4 yv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int hh = 0; hh < H; ++hh) {
             const f4 oo = sO[buf][hh][lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ya[hh & 3] = mfma4(sWoh[4 * hh + r][lane], oo[r], ya[hh & 3]);
+            for (int r = 0; r < 4; ++r) yv = mfma4(sWoh[4 * hh + r][lane], oo[r], yv);
         }
-        const f4 yv = (ya[0] + ya[1]) + (ya[2] + ya[3]);
         const int a = 16 * qt + li;
-        if (a < n) {
-            const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
-            if (row >= 0 && row < A.n_edges)
-                *reinterpret_cast<f4*>(A.y + row * C + 16 * h + 4 * g) = yv;
+        if (last) {
+            if (a < n) {
+                const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+                if (row >= 0 && row < A.n_edges)
+                    *reinterpret_cast<f4*>(A.y + row * C + 16 * h + 4 * g) = yv;
+            }
+        } else {
+            const f4 zero = {0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f4*>(&sX[a][16 * h + 4 * g]) = a < n ? yv : zero;
         }
     }
 }
@@ -205,7 +223,8 @@ template <int H, int TMAX>
 __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
     constexpr int C = 16 * H;
     constexpr int KS = C / 4;
-    __shared__ f4 sQ[H][TMAX][64];
+    constexpr int NTH = 64 * H;
+    __shared__ float sX[16 * TMAX][Lds<H>::XS];
     __shared__ f4 sO[2][H][64];
     __shared__ float sWo[H][KS][64];
 
@@ -226,13 +245,42 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
             continue;
         }
         const int nt = (n + 15) >> 4;
+
+        // Gather the block: rows a < n from x (through `order`), zeros up to the tile edge.
+        // All loads of a thread are issued before any LDS write.
+        {
+            constexpr int CH = C / 4;                          // float4 chunks per row
+            constexpr int PER = (16 * TMAX * CH + NTH - 1) / NTH;
+            f4 v[PER];
+            const int chunks = 16 * nt * CH;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int idx = threadIdx.x + j * NTH;
+                const int a = idx / CH, c4 = idx % CH;
+                v[j] = f4{0.f, 0.f, 0.f, 0.f};
+                if (idx < chunks && a < n) {
+                    const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+                    if (row >= 0 && row < A.n_edges)
+                        v[j] = *reinterpret_cast<const f4*>(A.x + row * C + 4 * c4);
+                    else
+                        bad_index = true;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const int idx = threadIdx.x + j * NTH;
+                const int a = idx / CH, c4 = idx % CH;
+                if (idx < chunks) *reinterpret_cast<f4*>(&sX[a][4 * c4]) = v[j];
+            }
+        }
+        __syncthreads();
+
         for (int layer = 0; layer < A.layers; ++layer) {
-            const float* src = layer == 0 ? A.x : A.y;
             const float* P = A.w + (size_t)layer * 4 * C * C + ((size_t)h * 64 + lane) * KS;
-#define NGA_CASE(T)                                                                          \
-    case T:                                                                                  \
-        if constexpr (T <= TMAX)                                                             \
-            centre_layer<H, T>(A, src, P, r0, n, sQ[h], sO, sWo[h], lane, h, bad_index);     \
+            const bool last = layer == A.layers - 1;
+#define NGA_CASE(T)                                                                   \
+    case T:                                                                           \
+        if constexpr (T <= TMAX) centre_layer<H, T>(A, P, r0, n, last, sX, sO, sWo[h], lane, h); \
         break;
             switch (nt) {
                 NGA_CASE(1) NGA_CASE(2) NGA_CASE(3) NGA_CASE(4) NGA_CASE(5) NGA_CASE(6)
@@ -240,7 +288,7 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
                 default: break;
             }
 #undef NGA_CASE
-            __syncthreads();  // this layer's rows are stored before the next layer reads them
+            __syncthreads();  // the block (or this layer's rows) is complete before it is read
         }
     }
     if (bad_index) raise_bits(A.status, kBitIndex);
@@ -248,7 +296,10 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
 
 template <int H>
 int launch_h(int tmax, const FusedArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)a.n_centres), block(64 * H);
+    // One work-group per centre: the hardware keeps two resident per compute unit (LDS and
+    // registers) and starts the next as soon as one retires; the kernel's stride loop covers
+    // grids smaller than the centre count.
+    dim3 grid((unsigned)std::min<int64_t>(a.n_centres, INT32_MAX)), block(64 * H);
     if (tmax <= 4) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 4>), grid, block, 0, s, a);
     else if (tmax <= 8) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 8>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((fused_f32_d16_kernel<H, 12>), grid, block, 0, s, a);
