@@ -235,14 +235,15 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
         if (A.row_ptr[0] != 0 || A.row_ptr[A.n_centres] > A.n_edges) raise_bits(A.status, kBitCap);
     }
     bool bad_index = false;
-    for (int centre = blockIdx.x; centre < A.n_centres; centre += gridDim.x) {
+    {
+        const int centre = blockIdx.x;
         const int64_t r0 = A.row_ptr[centre];
         const int64_t r1 = A.row_ptr[centre + 1];
         const int n = (int)(r1 - r0);
-        if (n <= 0) continue;
+        if (n <= 0) return;
         if (n > A.nnei_cap || n > 16 * TMAX || r0 < 0 || r1 > A.n_edges) {
             if (threadIdx.x == 0) raise_bits(A.status, kBitCap);
-            continue;
+            return;
         }
         const int nt = (n + 15) >> 4;
 
@@ -297,9 +298,8 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
 template <int H>
 int launch_h(int tmax, const FusedArgs& a, hipStream_t s) {
     // One work-group per centre: the hardware keeps two resident per compute unit (LDS and
-    // registers) and starts the next as soon as one retires; the kernel's stride loop covers
-    // grids smaller than the centre count.
-    dim3 grid((unsigned)std::min<int64_t>(a.n_centres, INT32_MAX)), block(64 * H);
+    // registers) and starts the next as soon as one retires.
+    dim3 grid((unsigned)a.n_centres), block(64 * H);
     if (tmax <= 4) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 4>), grid, block, 0, s, a);
     else if (tmax <= 8) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 8>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((fused_f32_d16_kernel<H, 12>), grid, block, 0, s, a);
