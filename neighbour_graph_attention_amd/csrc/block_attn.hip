@@ -13,8 +13,11 @@
 //   qkv[s]  = x[order(s)] [Wq | Wk | Wv]           (row-gather GEMM)
 //   o[s]    = per-centre attention of qkv rows      (one work-group per centre)
 //   y[order(s)] = o[s] Wo                           (row-scatter GEMM)
-// The fused fp32 kernel for 16-wide heads lives in block_attn_fused.hip.
+// The fused fp32 kernel for 16-wide heads lives in block_attn_fused.hip and the fp64
+// matrix-core path for heads of width 8, 16 and 32 in block_attn_f64.hip; this path covers
+// every other shape.
 #include "nga_internal.h"
+#include "block_attn_f64.h"
 #include "block_attn_fused.h"
 
 namespace nga {
@@ -311,6 +314,7 @@ extern "C" size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t
 extern "C" const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads) {
     if (dtype != NGA_F64 && dtype != NGA_F32) return "unsupported";
     if (nga::use_fused(dtype, nnei_cap, c, n_heads)) return nga::fused_name(dtype, c, n_heads);
+    if (dtype == NGA_F64 && nga::f64_mfma_supported(nnei_cap, c, n_heads)) return "mfma_f64";
     return dtype == NGA_F64 ? "generic_f64" : "generic_f32";
 }
 
@@ -349,6 +353,13 @@ extern "C" int block_attn_forward(int dtype, const int64_t* row_ptr, const int32
                        status);
     int rc = last_launch_status();
     if (rc) return rc;
+    if (dtype == NGA_F64 && f64_mfma_supported(nnei_cap, c, n_heads)) {
+        GenericWs w = carve_generic(ws, n_edges, c, n_layers, sizeof(double));
+        return run_f64_mfma(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
+                            static_cast<const double*>(weights), static_cast<const double*>(x),
+                            static_cast<double*>(y), static_cast<double*>(w.qkv),
+                            static_cast<double*>(w.o), static_cast<double*>(w.xbuf), status, s);
+    }
     if (dtype == NGA_F64)
         return run_generic<double>(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads,
                                    n_layers, static_cast<const double*>(weights),

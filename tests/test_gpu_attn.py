@@ -88,6 +88,10 @@ CASES = [
     (np.float64, 50, 45, 32, 4, 3, 3),
     (np.float64, 20, 33, 24, 3, 1, 4),
     (np.float64, 10, 70, 8, 1, 2, 5),
+    (np.float64, 30, 128, 64, 4, 2, 11),     # head width 16, rows up to the 128 cap
+    (np.float64, 20, 150, 32, 4, 1, 12),     # rows past 128: generic path
+    (np.float64, 20, 30, 20, 2, 2, 13),      # head width 10: generic path
+    (np.float32, 20, 60, 40, 5, 1, 14),      # 5 heads of 8: generic path
     (np.float32, 60, 181, 64, 4, 2, 6),
     (np.float32, 40, 176, 64, 4, 1, 7),
     (np.float32, 40, 96, 32, 2, 1, 8),
@@ -130,7 +134,8 @@ def test_order_gather_scatter(oracle_mod, dtype, c, heads, cap):
     assert _normwise(y2[perm].astype(np.float64), ref) < TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float64, 32, 4, 40), (np.float32, 64, 4, 181)])
+@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float64, 32, 4, 40), (np.float64, 128, 4, 110),
+                                             (np.float32, 64, 4, 181)])
 def test_deterministic_and_cap_independent(dtype, c, heads, cap):
     rp = W.random_rows(50, cap, 91)
     e = int(rp[-1])
@@ -146,7 +151,7 @@ def test_deterministic_and_cap_independent(dtype, c, heads, cap):
     assert np.array_equal(a, c2)
 
 
-PATH_CASES = [(np.float64, 4), (np.float32, 1)]  # generic path, fused path
+PATH_CASES = [(np.float64, 4), (np.float64, 2), (np.float32, 1)]  # generic, mfma_f64, fused
 
 
 @pytest.mark.parametrize("dtype,heads", PATH_CASES)
