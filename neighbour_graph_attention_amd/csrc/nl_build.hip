@@ -12,10 +12,11 @@
 //   2. bin: validate each position, cell id, atomic slot within the cell
 //   3. exclusive scan of cell counts -> cell offsets (scan.hip)
 //   4. scatter atoms into cell order (positions copied bit for bit)
-//   5. select: one work-group per (cell, split); the candidates of the cell's stencil are
-//      staged in LDS; each wavefront takes one centre at a time, evaluates the fp64 distance
-//      of every candidate, compacts the accepted ones with ballot/mbcnt into a per-wave LDS
-//      list, sorts them in registers (bitonic, 128-bit keys (r2 bits, j, shift)) and writes
+//   5. select: one work-group per (cell, split) with the cell's stencil table in LDS; each
+//      wavefront takes one centre at a time, reads the stencil cells' cell-sorted positions
+//      with coalesced loads, evaluates the fp64 distance of every candidate, compacts the
+//      accepted ones with ballot/mbcnt into a per-wave LDS list, sorts them in registers
+//      (bitonic on the r2 bit patterns, then exact ties re-ranked by (j, shift)) and writes
 //      the first min(sel, count) as the row.
 //
 // The distance is d = (x_j - x_i) + n*L per axis, r2 = (dx*dx + dy*dy) + dz*dz, in IEEE
@@ -31,9 +32,7 @@ namespace {
 
 constexpr int kNlBlock = 256;
 constexpr int kNlWaves = kNlBlock / 64;
-constexpr int kNlStage = 1024;   // stencil candidates staged in LDS per work-group
 constexpr int kMaxReach = 5;     // stencil reach (cells) per side
-constexpr int kMaxStencil = (2 * kMaxReach + 1) * (2 * kMaxReach + 1) * (2 * kMaxReach + 1);
 constexpr double kCellSlack = 1e-9;  // cells are at least rcut * (1 + slack) wide
 constexpr int kMaxCellsPerAxis = 1024;
 
@@ -182,46 +181,38 @@ struct Stencil {
     int cx, cy, cz;
 };
 
+// floor(r / nc) for nc > 0.
+__device__ inline int floor_div(int r, int nc) { return r >= 0 ? r / nc : -((-r + nc - 1) / nc); }
+
 // Stencil entry s of the cell (cx, cy, cz): neighbour cell and image shift.
-__device__ inline void stencil_entry(const Geom& g, const Stencil& st, int s, int* wcell,
-                                     int* code) {
-    const int wx = 2 * g.reach[0] + 1, wy = 2 * g.reach[1] + 1;
-    int ox = s % wx - g.reach[0];
-    int oy = (s / wx) % wy - g.reach[1];
-    int oz = s / (wx * wy) - g.reach[2];
-    int r[3] = {st.cx + ox, st.cy + oy, st.cz + oz};
-    int w[3], nsh[3];
-    for (int a = 0; a < 3; ++a) {
-        int q = r[a] >= 0 ? r[a] / g.nc[a] : -((-r[a] + g.nc[a] - 1) / g.nc[a]);  // floor
-        nsh[a] = q;
-        w[a] = r[a] - q * g.nc[a];
-    }
-    *wcell = (w[2] * g.nc[1] + w[1]) * g.nc[0] + w[0];
-    *code = pack_shift(nsh[0], nsh[1], nsh[2]);
+__device__ inline void stencil_entry(int ncx, int ncy, int ncz, int kx, int ky, int kz,
+                                     const Stencil& st, int s, int* wcell, int* code) {
+    const int wx = 2 * kx + 1, wy = 2 * ky + 1;
+    const int rx = st.cx + s % wx - kx;
+    const int ry = st.cy + (s / wx) % wy - ky;
+    const int rz = st.cz + s / (wx * wy) - kz;
+    const int nx = floor_div(rx, ncx), ny = floor_div(ry, ncy), nz = floor_div(rz, ncz);
+    *wcell = ((rz - nz * ncz) * ncy + (ry - ny * ncy)) * ncx + (rx - nx * ncx);
+    *code = pack_shift(nx, ny, nz);
 }
 
-// Largest s with segoff[s] <= t (segoff is non-decreasing, segoff[0] = 0 <= t).
-__device__ inline int find_segment(const int* segoff, int S, int t) {
-    int lo = 0, hi = S;  // invariant: segoff[lo] <= t < segoff[hi]
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (segoff[mid] <= t) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
-struct Key {
-    uint64_t hi;  // bit pattern of r2 (r2 >= 0, so bit order is numeric order)
-    uint64_t lo;  // (j << 24) | shift code
+// Per-wavefront candidate list in LDS: r2 bit patterns, neighbour index, shift code, and the
+// list index each sorted position came from.
+struct WaveList {
+    uint64_t r2[NGA_ROW_CAP];
+    int32_t j[NGA_ROW_CAP];
+    int32_t code[NGA_ROW_CAP];
+    int32_t pay[NGA_ROW_CAP];
 };
 
-__device__ inline bool key_less(const Key& a, const Key& b) {
-    return a.hi < b.hi || (a.hi == b.hi && a.lo < b.lo);
+__device__ inline uint64_t lo_key(const WaveList& L, int p) {
+    return ((uint64_t)(uint32_t)L.j[p] << 24) | (uint64_t)(uint32_t)L.code[p];
 }
 
-// Bitonic sort of 64*NS keys held NS per lane (element e = lane*NS + q), ascending.
+// Bitonic sort of 64*NS (key, payload) pairs held NS per lane (element e = lane*NS + q),
+// ascending by key.  Equal keys end in an unspecified order; the caller resolves them.
 template <int NS>
-__device__ inline void bitonic_sort(Key (&k)[NS], int lane) {
+__device__ inline void bitonic_sort(uint64_t (&k)[NS], int (&p)[NS], int lane) {
     constexpr int M = 64 * NS;
 #pragma unroll
     for (int size = 2; size <= M; size <<= 1) {
@@ -231,11 +222,12 @@ __device__ inline void bitonic_sort(Key (&k)[NS], int lane) {
 #pragma unroll
                 for (int q = 0; q < NS; ++q) {
                     if (q & stride) continue;
-                    const int p = q | stride;
+                    const int o = q | stride;
                     const int e = lane * NS + q;
                     const bool ascending = (e & size) == 0;
-                    if (key_less(k[p], k[q]) == ascending) {
-                        Key t = k[q]; k[q] = k[p]; k[p] = t;
+                    if ((k[o] < k[q]) == ascending) {
+                        const uint64_t tk = k[q]; k[q] = k[o]; k[o] = tk;
+                        const int tp = p[q]; p[q] = p[o]; p[o] = tp;
                     }
                 }
             } else {
@@ -243,51 +235,15 @@ __device__ inline void bitonic_sort(Key (&k)[NS], int lane) {
 #pragma unroll
                 for (int q = 0; q < NS; ++q) {
                     const int e = lane * NS + q;
-                    Key o;
-                    o.hi = __shfl_xor(k[q].hi, lx, 64);
-                    o.lo = __shfl_xor(k[q].lo, lx, 64);
+                    const uint64_t ok = __shfl_xor(k[q], lx, 64);
+                    const int op = __shfl_xor(p[q], lx, 64);
                     const bool ascending = (e & size) == 0;
                     const bool lower = (e & stride) == 0;
-                    const bool keep_min = (ascending == lower);
-                    const bool o_less = key_less(o, k[q]);
-                    if (o_less == keep_min) k[q] = o;
+                    const bool take = lower == ascending ? ok < k[q] : k[q] < ok;
+                    if (take) { k[q] = ok; p[q] = op; }
                 }
             }
         }
-    }
-}
-
-template <int NS>
-__device__ void sort_and_write(const Key* list, int count, int keep, int i, int lane,
-                               const SelectArgs& A) {
-    Key k[NS];
-#pragma unroll
-    for (int q = 0; q < NS; ++q) {
-        int e = lane * NS + q;
-        if (e < count) k[q] = list[e];
-        else { k[q].hi = ~0ull; k[q].lo = ~0ull; }
-    }
-    bitonic_sort<NS>(k, lane);
-    int32_t* row = A.nbr + (int64_t)i * A.sel;
-    int32_t* rsh = A.nbr_shift + (int64_t)i * A.sel * 3;
-#pragma unroll
-    for (int q = 0; q < NS; ++q) {
-        int e = lane * NS + q;
-        if (e >= A.sel) continue;
-        if (e < keep) {
-            int code = (int)(k[q].lo & 0xffffff);
-            row[e] = (int32_t)(k[q].lo >> 24);
-            rsh[3 * e + 0] = shift_x(code);
-            rsh[3 * e + 1] = shift_y(code);
-            rsh[3 * e + 2] = shift_z(code);
-        } else {
-            row[e] = -1;
-            rsh[3 * e + 0] = 0; rsh[3 * e + 1] = 0; rsh[3 * e + 2] = 0;
-        }
-    }
-    for (int e = 64 * NS + lane; e < A.sel; e += 64) {
-        row[e] = -1;
-        rsh[3 * e + 0] = 0; rsh[3 * e + 1] = 0; rsh[3 * e + 2] = 0;
     }
 }
 
@@ -297,126 +253,183 @@ __device__ inline void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Sort the wave's `count` candidates by (r2, j, shift) and write the first `keep` as row i.
+// The bitonic network orders the r2 bit patterns; positions whose r2 equals a neighbour's
+// (exact ties, e.g. on ideal lattices) are then re-ranked within their run by (j, shift).
+template <int NS>
+__device__ void sort_and_write(WaveList& L, int count, int keep, int sel, int32_t* row,
+                               int32_t* rsh, int lane) {
+    uint64_t k[NS];
+    int p[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        const int e = lane * NS + q;
+        k[q] = e < count ? L.r2[e] : ~0ull;
+        p[q] = e;
+    }
+    bitonic_sort<NS>(k, p, lane);
+
+    // Ties among real entries: compare with the previous sorted position.
+    const uint64_t prev_last = __shfl_up(k[NS - 1], 1, 64);
+    bool tie = false;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        const int e = lane * NS + q;
+        const uint64_t before = q > 0 ? k[q - 1] : prev_last;
+        if (e > 0 && e < count && before == k[q]) tie = true;
+    }
+    int pos[NS];
+#pragma unroll
+    for (int q = 0; q < NS; ++q) pos[q] = lane * NS + q;
+    if (__ballot(tie)) {
+        // Rare path: publish the sorted keys and payloads, then rank each tied entry inside
+        // its run by (j, shift).  r2[] is free to overwrite: payloads index j[] and code[].
+        wave_sync_lds();
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const int e = lane * NS + q;
+            if (e < count) { L.r2[e] = k[q]; L.pay[e] = p[q]; }
+        }
+        wave_sync_lds();
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            const int e = lane * NS + q;
+            if (e >= count) continue;
+            int rs = e, re = e + 1;
+            while (rs > 0 && L.r2[rs - 1] == k[q]) --rs;
+            while (re < count && L.r2[re] == k[q]) ++re;
+            if (re - rs == 1) continue;
+            const uint64_t mine = lo_key(L, p[q]);
+            int rank = 0;
+            for (int t = rs; t < re; ++t) rank += lo_key(L, L.pay[t]) < mine;
+            pos[q] = rs + rank;
+        }
+    }
+
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+        const int e = lane * NS + q;
+        if (e < count) {
+            const int at = pos[q];
+            if (at < keep) {
+                const int code = L.code[p[q]];
+                row[at] = L.j[p[q]];
+                rsh[3 * at + 0] = shift_x(code);
+                rsh[3 * at + 1] = shift_y(code);
+                rsh[3 * at + 2] = shift_z(code);
+            }
+        } else if (e < sel) {
+            row[e] = -1;
+            rsh[3 * e + 0] = 0; rsh[3 * e + 1] = 0; rsh[3 * e + 2] = 0;
+        }
+    }
+    for (int e = 64 * NS + lane; e < sel; e += 64) {
+        row[e] = -1;
+        rsh[3 * e + 0] = 0; rsh[3 * e + 1] = 0; rsh[3 * e + 2] = 0;
+    }
+}
+
+// One work-group per (cell, split).  The cell's stencil (start, length, shift code per
+// neighbour cell) goes to LDS once; then each wavefront takes one centre of the cell at a
+// time and walks the stencil cells, reading their cell-sorted positions with coalesced
+// loads, testing the pinned fp64 distance and compacting the accepted candidates into its
+// LDS list with ballot / mbcnt.
 __global__ void __launch_bounds__(kNlBlock)
 select_kernel(SelectArgs A) {
-    __shared__ double s_x[kNlStage], s_y[kNlStage], s_z[kNlStage];
-    __shared__ int s_j[kNlStage], s_code[kNlStage];
-    __shared__ int s_segoff[kMaxStencil + 1];
-    __shared__ Key s_list[kNlWaves][NGA_ROW_CAP];
+    extern __shared__ __align__(16) unsigned char nl_smem[];
+    WaveList* lists = reinterpret_cast<WaveList*>(nl_smem);
+    int* s_start = reinterpret_cast<int*>(nl_smem + kNlWaves * sizeof(WaveList));
+    int* s_len = s_start + A.g.stencil;
+    int* s_code = s_len + A.g.stencil;
 
-    const Geom& g = A.g;
+    const int ncx = A.g.nc[0], ncy = A.g.nc[1], ncz = A.g.nc[2];
     const int cell = blockIdx.x;
     const int c0 = (int)A.cell_start[cell];
     const int c1 = (int)A.cell_start[cell + 1];
     if (c0 == c1 || (int)blockIdx.y * kNlWaves >= c1 - c0) return;  // uniform per block
 
     Stencil st;
-    st.cx = cell % g.nc[0];
-    st.cy = (cell / g.nc[0]) % g.nc[1];
-    st.cz = cell / (g.nc[0] * g.nc[1]);
-    const int S = g.stencil;
-
-    // Segment lengths of the stencil, then their exclusive prefix (one wavefront).
-    for (int s = threadIdx.x; s < S; s += kNlBlock) {
+    st.cx = cell % ncx;
+    st.cy = (cell / ncx) % ncy;
+    st.cz = cell / (ncx * ncy);
+    const int S = A.g.stencil;
+    for (int e = threadIdx.x; e < S; e += kNlBlock) {
         int w, code;
-        stencil_entry(g, st, s, &w, &code);
-        s_segoff[s + 1] = (int)(A.cell_start[w + 1] - A.cell_start[w]);
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const int lane = threadIdx.x;
-        int carry = 0;
-        if (lane == 0) s_segoff[0] = 0;
-        for (int base = 0; base < S; base += 64) {
-            int s = base + lane;
-            int v = s < S ? s_segoff[s + 1] : 0;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                int o = __shfl_up(v, d, 64);
-                if (lane >= d) v += o;
-            }
-            if (s < S) s_segoff[s + 1] = carry + v;
-            carry += __shfl(v, 63, 64);
-        }
-    }
-    __syncthreads();
-    const int T = s_segoff[S];
-
-    // Stage the first kNlStage candidates (positions bit for bit, index, shift code).
-    const int staged = T < kNlStage ? T : kNlStage;
-    for (int t = threadIdx.x; t < staged; t += kNlBlock) {
-        int s = find_segment(s_segoff, S, t);
-        int w, code;
-        stencil_entry(g, st, s, &w, &code);
-        int64_t a = A.cell_start[w] + (t - s_segoff[s]);
-        s_x[t] = A.sx[a];
-        s_y[t] = A.sy[a];
-        s_z[t] = A.sz[a];
-        s_j[t] = A.sidx[a];
-        s_code[t] = code;
+        stencil_entry(ncx, ncy, ncz, A.g.reach[0], A.g.reach[1], A.g.reach[2], st, e, &w, &code);
+        const int64_t b = A.cell_start[w];
+        s_start[e] = (int)b;
+        s_len[e] = (int)(A.cell_start[w + 1] - b);
+        s_code[e] = code;
     }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    Key* list = s_list[wave];
+    WaveList& L = lists[wave];
     const int zero_code = (128 << 16) | (128 << 8) | 128;
-    const double Lx = g.L[0], Ly = g.L[1], Lz = g.L[2];
+    const double Lx = A.g.L[0], Ly = A.g.L[1], Lz = A.g.L[2];
+    const double rc2 = A.rc2;
+    const int sel = A.sel;
+    const double* __restrict__ sx = A.sx;
+    const double* __restrict__ sy = A.sy;
+    const double* __restrict__ sz = A.sz;
+    const int32_t* __restrict__ sidx = A.sidx;
 
     for (int li = blockIdx.y * kNlWaves + wave; li < c1 - c0; li += kNlWaves * A.nsplit) {
         const int ci = c0 + li;
-        const int i = A.sidx[ci];
-        const double xi = A.sx[ci], yi = A.sy[ci], zi = A.sz[ci];
+        const int i = sidx[ci];
+        const double xi = sx[ci], yi = sy[ci], zi = sz[ci];
         int count = 0;
-        for (int base = 0; base < T; base += 64) {
-            const int t = base + lane;
-            bool accept = false;
-            double r2 = 0.0;
-            int j = 0, code = 0;
-            if (t < T) {
-                double xj, yj, zj;
-                if (t < kNlStage) {
-                    xj = s_x[t]; yj = s_y[t]; zj = s_z[t];
-                    j = s_j[t]; code = s_code[t];
-                } else {
-                    int s = find_segment(s_segoff, S, t);
-                    int w;
-                    stencil_entry(g, st, s, &w, &code);
-                    int64_t a = A.cell_start[w] + (t - s_segoff[s]);
-                    xj = A.sx[a]; yj = A.sy[a]; zj = A.sz[a];
-                    j = A.sidx[a];
+        for (int sc = 0; sc < S; ++sc) {
+            const int base = s_start[sc], len = s_len[sc], code = s_code[sc];
+            const double nx = (double)shift_x(code) * Lx;
+            const double ny = (double)shift_y(code) * Ly;
+            const double nz = (double)shift_z(code) * Lz;
+            for (int t0 = 0; t0 < len; t0 += 64) {
+                const int t = t0 + lane;
+                bool accept = false;
+                double r2 = 0.0;
+                int j = 0;
+                if (t < len) {
+                    const int a = base + t;
+                    const double dx = (sx[a] - xi) + nx;
+                    const double dy = (sy[a] - yi) + ny;
+                    const double dz = (sz[a] - zi) + nz;
+                    const double sxy = dx * dx + dy * dy;
+                    r2 = sxy + dz * dz;
+                    j = sidx[a];
+                    accept = (r2 < rc2) && !(j == i && code == zero_code);
                 }
-                const double dx = (xj - xi) + (double)shift_x(code) * Lx;
-                const double dy = (yj - yi) + (double)shift_y(code) * Ly;
-                const double dz = (zj - zi) + (double)shift_z(code) * Lz;
-                const double sxy = dx * dx + dy * dy;
-                r2 = sxy + dz * dz;
-                accept = (r2 < A.rc2) && !(j == i && code == zero_code);
+                const uint64_t m = __ballot(accept);
+                const int slot = count + __popcll(m & lt_mask);
+                if (accept && slot < NGA_ROW_CAP) {
+                    L.r2[slot] = (uint64_t)__double_as_longlong(r2);
+                    L.j[slot] = j;
+                    L.code[slot] = code;
+                }
+                count += __popcll(m);
             }
-            const uint64_t m = __ballot(accept);
-            const int slot = count + __popcll(m & lt_mask);
-            if (accept && slot < NGA_ROW_CAP) {
-                Key k;
-                k.hi = (uint64_t)__double_as_longlong(r2);
-                k.lo = ((uint64_t)(uint32_t)j << 24) | (uint64_t)code;
-                list[slot] = k;
-            }
-            count += __popcll(m);
         }
         wave_sync_lds();
         if (count > NGA_ROW_CAP) {
             if (lane == 0) raise_bits(A.status, kBitRowCap);
             count = 0;
         }
-        const int keep = count < A.sel ? count : A.sel;
-        if (count <= 64) sort_and_write<1>(list, count, keep, i, lane, A);
-        else if (count <= 128) sort_and_write<2>(list, count, keep, i, lane, A);
-        else if (count <= 256) sort_and_write<4>(list, count, keep, i, lane, A);
-        else sort_and_write<8>(list, count, keep, i, lane, A);
+        const int keep = count < sel ? count : sel;
+        int32_t* row = A.nbr + (int64_t)i * sel;
+        int32_t* rsh = A.nbr_shift + (int64_t)i * sel * 3;
+        if (count <= 64) sort_and_write<1>(L, count, keep, sel, row, rsh, lane);
+        else if (count <= 128) sort_and_write<2>(L, count, keep, sel, row, rsh, lane);
+        else if (count <= 256) sort_and_write<4>(L, count, keep, sel, row, rsh, lane);
+        else sort_and_write<8>(L, count, keep, sel, row, rsh, lane);
         if (lane == 0) A.nnei[i] = keep;
         wave_sync_lds();
     }
+}
+
+size_t select_lds_bytes(const Geom& g) {
+    return kNlWaves * sizeof(WaveList) + 3 * sizeof(int) * (size_t)g.stencil;
 }
 
 int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t sel,
@@ -449,7 +462,7 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
     A.status = status;
     hipLaunchKernelGGL(select_kernel, dim3((unsigned)g.ncells, (unsigned)A.nsplit), dim3(kNlBlock),
-                       0, s, A);
+                       (unsigned)select_lds_bytes(g), s, A);
     return last_launch_status();
 }
 
