@@ -16,8 +16,8 @@
 //      wavefront takes one centre at a time, reads the stencil cells' cell-sorted positions
 //      with coalesced loads, evaluates the fp64 distance of every candidate, compacts the
 //      accepted ones with ballot/mbcnt into a per-wave LDS list, sorts them in registers
-//      (bitonic on the r2 bit patterns, then exact ties re-ranked by (j, shift)) and writes
-//      the first min(sel, count) as the row.
+//      (bitonic on the upper 32 bits of the r2 bit pattern, then near-equal runs re-ranked
+//      by the full key (r2, j, shift)) and writes the first min(sel, count) as the row.
 //
 // The distance is d = (x_j - x_i) + n*L per axis, r2 = (dx*dx + dy*dy) + dz*dz, in IEEE
 // fp64 with contraction disabled in this file, so every accepted r2 is bit-identical to a
@@ -209,10 +209,9 @@ __device__ inline uint64_t lo_key(const WaveList& L, int p) {
     return ((uint64_t)(uint32_t)L.j[p] << 24) | (uint64_t)(uint32_t)L.code[p];
 }
 
-// Bitonic sort of 64*NS (key, payload) pairs held NS per lane (element e = lane*NS + q),
-// ascending by key.  Equal keys end in an unspecified order; the caller resolves them.
+// Bitonic sort of 64*NS 64-bit words held NS per lane (element e = lane*NS + q), ascending.
 template <int NS>
-__device__ inline void bitonic_sort(uint64_t (&k)[NS], int (&p)[NS], int lane) {
+__device__ inline void bitonic_sort(uint64_t (&k)[NS], int lane) {
     constexpr int M = 64 * NS;
 #pragma unroll
     for (int size = 2; size <= M; size <<= 1) {
@@ -226,8 +225,7 @@ __device__ inline void bitonic_sort(uint64_t (&k)[NS], int (&p)[NS], int lane) {
                     const int e = lane * NS + q;
                     const bool ascending = (e & size) == 0;
                     if ((k[o] < k[q]) == ascending) {
-                        const uint64_t tk = k[q]; k[q] = k[o]; k[o] = tk;
-                        const int tp = p[q]; p[q] = p[o]; p[o] = tp;
+                        const uint64_t t = k[q]; k[q] = k[o]; k[o] = t;
                     }
                 }
             } else {
@@ -236,11 +234,10 @@ __device__ inline void bitonic_sort(uint64_t (&k)[NS], int (&p)[NS], int lane) {
                 for (int q = 0; q < NS; ++q) {
                     const int e = lane * NS + q;
                     const uint64_t ok = __shfl_xor(k[q], lx, 64);
-                    const int op = __shfl_xor(p[q], lx, 64);
                     const bool ascending = (e & size) == 0;
                     const bool lower = (e & stride) == 0;
                     const bool take = lower == ascending ? ok < k[q] : k[q] < ok;
-                    if (take) { k[q] = ok; p[q] = op; }
+                    if (take) k[q] = ok;
                 }
             }
         }
@@ -253,55 +250,60 @@ __device__ inline void wave_sync_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Full key of list entry p, compared as (r2 bit pattern, j, shift code).
+__device__ inline bool full_less(const WaveList& L, int a, int b) {
+    if (L.r2[a] != L.r2[b]) return L.r2[a] < L.r2[b];
+    return lo_key(L, a) < lo_key(L, b);
+}
+
 // Sort the wave's `count` candidates by (r2, j, shift) and write the first `keep` as row i.
-// The bitonic network orders the r2 bit patterns; positions whose r2 equals a neighbour's
-// (exact ties, e.g. on ideal lattices) are then re-ranked within their run by (j, shift).
+// The bitonic network sorts one 64-bit word per candidate: the upper 32 bits of the r2 bit
+// pattern above the list index.  Entries whose upper 32 bits equal a neighbour's are then
+// re-ranked inside their run by the full key (rare: it takes r2 values equal to about 1e-6
+// relative, such as the exact ties of ideal lattices).
 template <int NS>
 __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, int32_t* row,
                                int32_t* rsh, int lane) {
     uint64_t k[NS];
-    int p[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         const int e = lane * NS + q;
-        k[q] = e < count ? L.r2[e] : ~0ull;
-        p[q] = e;
+        k[q] = e < count ? ((L.r2[e] >> 32) << 32) | (uint64_t)e : ~0ull;
     }
-    bitonic_sort<NS>(k, p, lane);
+    bitonic_sort<NS>(k, lane);
 
-    // Ties among real entries: compare with the previous sorted position.
     const uint64_t prev_last = __shfl_up(k[NS - 1], 1, 64);
     bool tie = false;
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         const int e = lane * NS + q;
         const uint64_t before = q > 0 ? k[q - 1] : prev_last;
-        if (e > 0 && e < count && before == k[q]) tie = true;
+        if (e > 0 && e < count && (before >> 32) == (k[q] >> 32)) tie = true;
     }
     int pos[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) pos[q] = lane * NS + q;
     if (__ballot(tie)) {
-        // Rare path: publish the sorted keys and payloads, then rank each tied entry inside
-        // its run by (j, shift).  r2[] is free to overwrite: payloads index j[] and code[].
-        wave_sync_lds();
+        // Publish the sorted list indices, then rank each entry of a run of equal upper
+        // words by the full key.
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
             const int e = lane * NS + q;
-            if (e < count) { L.r2[e] = k[q]; L.pay[e] = p[q]; }
+            if (e < count) L.pay[e] = (int)(uint32_t)k[q];
         }
         wave_sync_lds();
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
             const int e = lane * NS + q;
             if (e >= count) continue;
+            const uint32_t hi = (uint32_t)(k[q] >> 32);
+            const int me = (int)(uint32_t)k[q];
             int rs = e, re = e + 1;
-            while (rs > 0 && L.r2[rs - 1] == k[q]) --rs;
-            while (re < count && L.r2[re] == k[q]) ++re;
+            while (rs > 0 && (uint32_t)(L.r2[L.pay[rs - 1]] >> 32) == hi) --rs;
+            while (re < count && (uint32_t)(L.r2[L.pay[re]] >> 32) == hi) ++re;
             if (re - rs == 1) continue;
-            const uint64_t mine = lo_key(L, p[q]);
             int rank = 0;
-            for (int t = rs; t < re; ++t) rank += lo_key(L, L.pay[t]) < mine;
+            for (int t = rs; t < re; ++t) rank += full_less(L, L.pay[t], me);
             pos[q] = rs + rank;
         }
     }
@@ -312,8 +314,9 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, int32_
         if (e < count) {
             const int at = pos[q];
             if (at < keep) {
-                const int code = L.code[p[q]];
-                row[at] = L.j[p[q]];
+                const int p = (int)(uint32_t)k[q];
+                const int code = L.code[p];
+                row[at] = L.j[p];
                 rsh[3 * at + 0] = shift_x(code);
                 rsh[3 * at + 1] = shift_y(code);
                 rsh[3 * at + 2] = shift_z(code);
@@ -362,6 +365,27 @@ select_kernel(SelectArgs A) {
         s_code[e] = code;
     }
     __syncthreads();
+    // Merge stencil cells that follow each other in memory with the same image shift (the
+    // cells of one x-row away from the box edge) into one segment.
+    __shared__ int s_nseg;
+    if (threadIdx.x == 0) {
+        int nseg = 0;
+        for (int e = 0; e < S; ++e) {
+            const int b = s_start[e], l = s_len[e], code = s_code[e];
+            if (l == 0) continue;
+            if (nseg > 0 && s_code[nseg - 1] == code && s_start[nseg - 1] + s_len[nseg - 1] == b) {
+                s_len[nseg - 1] += l;
+            } else {
+                s_start[nseg] = b;
+                s_len[nseg] = l;
+                s_code[nseg] = code;
+                ++nseg;
+            }
+        }
+        s_nseg = nseg;
+    }
+    __syncthreads();
+    const int nseg = s_nseg;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -381,34 +405,45 @@ select_kernel(SelectArgs A) {
         const int i = sidx[ci];
         const double xi = sx[ci], yi = sy[ci], zi = sz[ci];
         int count = 0;
-        for (int sc = 0; sc < S; ++sc) {
+        for (int sc = 0; sc < nseg; ++sc) {
             const int base = s_start[sc], len = s_len[sc], code = s_code[sc];
             const double nx = (double)shift_x(code) * Lx;
             const double ny = (double)shift_y(code) * Ly;
             const double nz = (double)shift_z(code) * Lz;
-            for (int t0 = 0; t0 < len; t0 += 64) {
-                const int t = t0 + lane;
-                bool accept = false;
-                double r2 = 0.0;
-                int j = 0;
-                if (t < len) {
-                    const int a = base + t;
-                    const double dx = (sx[a] - xi) + nx;
-                    const double dy = (sy[a] - yi) + ny;
-                    const double dz = (sz[a] - zi) + nz;
+            // Three chunks of 64 candidates per round: every load is issued before the first
+            // distance is evaluated.
+            for (int t0 = 0; t0 < len; t0 += 3 * 64) {
+                double cx[3], cy[3], cz[3];
+                int cj[3];
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    const int t = t0 + 64 * u + lane;
+                    const int a = base + (t < len ? t : 0);
+                    cx[u] = sx[a];
+                    cy[u] = sy[a];
+                    cz[u] = sz[a];
+                    cj[u] = sidx[a];
+                }
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    if (t0 + 64 * u >= len) break;  // uniform
+                    const int t = t0 + 64 * u + lane;
+                    const double dx = (cx[u] - xi) + nx;
+                    const double dy = (cy[u] - yi) + ny;
+                    const double dz = (cz[u] - zi) + nz;
                     const double sxy = dx * dx + dy * dy;
-                    r2 = sxy + dz * dz;
-                    j = sidx[a];
-                    accept = (r2 < rc2) && !(j == i && code == zero_code);
+                    const double r2 = sxy + dz * dz;
+                    const int j = cj[u];
+                    const bool accept = t < len && (r2 < rc2) && !(j == i && code == zero_code);
+                    const uint64_t m = __ballot(accept);
+                    const int slot = count + __popcll(m & lt_mask);
+                    if (accept && slot < NGA_ROW_CAP) {
+                        L.r2[slot] = (uint64_t)__double_as_longlong(r2);
+                        L.j[slot] = j;
+                        L.code[slot] = code;
+                    }
+                    count += __popcll(m);
                 }
-                const uint64_t m = __ballot(accept);
-                const int slot = count + __popcll(m & lt_mask);
-                if (accept && slot < NGA_ROW_CAP) {
-                    L.r2[slot] = (uint64_t)__double_as_longlong(r2);
-                    L.j[slot] = j;
-                    L.code[slot] = code;
-                }
-                count += __popcll(m);
             }
         }
         wave_sync_lds();
