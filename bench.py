@@ -27,7 +27,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "atoms/s for NL build + block-dense neighbour attention fwd; % of roofline"
-PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6}   # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0}   # MI355X dense MFMA peaks
+# The fused fp32 kernel runs its projections on the f16 matrix cores as (hi, lo) f16 pairs:
+# four f16 products per fp32 multiply-add.
+SPLIT_F16_FACTOR = 4.0
 PEAK_HBM_GBS = 8000.0                        # MI355X HBM3E
 
 
@@ -188,9 +191,22 @@ def main():
         torch.cuda.synchronize(dev)
 
     counts = np.diff(rp).astype(np.float64)
-    flops = w.layers * float(np.sum(8.0 * w.c * w.c * counts + 4.0 * w.c * counts * counts))
+    proj_flops = w.layers * float(np.sum(8.0 * w.c * w.c * counts))      # Q, K, V, O projections
+    attn_flops = w.layers * float(np.sum(4.0 * w.c * counts * counts))   # S = QK^T and O = PV
+    flops = proj_flops + attn_flops
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    if variant.startswith("fused_f32"):
+        # Matrix-core lower bound of this kernel: projections on the f16 pipe (split pairs),
+        # scores and values on the fp32 pipe; the peak is the flop rate at that bound.
+        t_min = (SPLIT_F16_FACTOR * proj_flops / PEAK_TFLOPS["f16"]
+                 + attn_flops / PEAK_TFLOPS["f32"]) / 1e12
+        peak = flops / t_min / 1e12
+        peak_basis = (f"projections as f16 hi/lo pairs ({SPLIT_F16_FACTOR:g} f16 flops per fp32 "
+                      f"flop at {PEAK_TFLOPS['f16']:g} TFLOP/s) + scores/values at "
+                      f"{PEAK_TFLOPS['f32']:g} TFLOP/s fp32")
+    else:
+        peak = PEAK_TFLOPS[w.dtype]
+        peak_basis = f"{w.dtype} dense MFMA"
     traffic = load_traffic(variant, w.name)
     nl_bytes = 24.0 * n + 8.0 * (n + 1) + 16.0 * e
     nl_gbs = nl_bytes / ((nl_ms + csr_ms) * 1e-3) / 1e9
@@ -213,7 +229,8 @@ def main():
                    "geometry_dtype": "f64", "attn_kernel": variant},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
-                     "kernel": variant, "flops_per_launch": flops, "launch_ms": attn_ms},
+                     "kernel": variant, "flops_per_launch": flops, "launch_ms": attn_ms,
+                     "peak_basis": peak_basis},
         "parts_ms": {"nl_build": nl_ms, "edge_csr": csr_ms, "block_attn_forward": attn_ms},
         "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
                    "frac": nl_gbs / PEAK_HBM_GBS},

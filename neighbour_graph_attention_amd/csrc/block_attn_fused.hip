@@ -1,4 +1,4 @@
-// Fused per-centre block attention, fp32, 16-wide heads, on CDNA matrix cores.
+// Fused per-centre block attention, fp32 results, 16-wide heads, on CDNA matrix cores.
 //
 // deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than dense ...", section
 // "Proposed fix: block-dense attention on the graph": gather a centre's (nnei, c) block
@@ -7,31 +7,48 @@
 // the block is gathered once into LDS, intermediate layers hand their output back through
 // the same LDS rows, and only the last layer writes to HBM.
 //
-// Work-group = H wavefronts, wavefront h owns head h (columns 16h .. 16h+15).  All
-// contractions are v_mfma_f32_16x16x4_f32.  Its operand / result layouts (A[i][k] from lane
-// i + 16k, B[k][j] from lane j + 16k, D[i][j] in lane j + 16*(i/4), register i%4) let every
-// result feed the next contraction directly, by choosing the order in which each
+// Work-group = H wavefronts, wavefront h owns head h (columns 16h .. 16h+15).
+//
+// Projections (Q, K, V from the block rows, Y from the heads' outputs) run on the f16 matrix
+// cores, v_mfma_f32_16x16x32_f16 with fp32 accumulation, on operands split into two f16
+// parts v = hi + lo after scaling by a power of two: the block's rows by 2^ex (one exponent
+// per centre and layer, max |x| 2^ex in [2^13, 2^14)), each weight matrix by its own 2^e,
+// the heads' outputs by 2^e_o (from the centre's max |V|, which bounds |O| because every O
+// row is a convex combination of V rows).  All four partial products go in: one MFMA takes
+// the weight's [hi, lo] parts against the activation's hi part (duplicated), a second one
+// against its lo part.  The pair of parts carries 22 significant bits; parts below the f16
+// normal range (the matrix cores flush f16 subnormals) lie under 2^-27 of the block's
+// maximum; every product is exact in the fp32 accumulator.  A 16-channel chunk then costs
+// two 16x16x32 f16 MFMAs (8 CU cycles at gfx950's dense f16 rate) where fp32 needs four
+// 16x16x4 MFMAs (32 CU cycles).  Scores S and the weighted values O stay on
+// v_mfma_f32_16x16x4_f32 with the projections' fp32 results as operands.
+//
+// Operand / result layouts.  f32 16x16x4: A[i][k] from lane i + 16k, B[k][j] from lane
+// j + 16k.  f16 16x16x32: A[i][k] from lane i + 16(k/8), element k%8, and B[k][j] from lane
+// j + 16(k/8), element k%8.  Both write D[i][j] to lane j + 16(i/4), register i%4.  Every
+// result feeds the next contraction directly, by choosing the order in which each
 // contraction walks its k index:
-//   projections  Q^T = Wq_h^T X^T, K^T = Wk_h^T X^T, V = X Wv_h   (k = input channel)
-//                with k(step kk, lane group g) = 16*(kk/4) + 4g + kk%4, so a lane reads
-//                four float4 of its own row of the block;
+//   projections  Q^T = Wq_h^T X^T, K^T = Wk_h^T X^T, V = X Wv_h: MFMA u covers input
+//                channels 16u + 4g + e (lane group g, e = 0..3): the weight operand holds
+//                their hi parts in elements 0..3 and lo parts in 4..7, the activation
+//                operand a part of the same four channels twice;
 //   scores       S^T = K Q^T, k = head channel 4g + r: A = K^T result register r,
 //                B = Q^T result register r;  lane (g, i) then holds query i against keys
 //                4g+r of every key tile;
 //   softmax      row max / sum over a lane's registers and the 4 lane groups (2 shuffles);
 //   values       O^T = V^T P^T, k = key 16kt + 4g + r: A = V result register r,
 //                B = P register r;
-//   output       Y^T = Wo^T [O_0 .. O_{H-1}]^T, k = 16hh + 4g + r: B = head hh's O^T
-//                register r, exchanged through LDS; lane (g, i) gets 4 consecutive output
-//                channels of row i, one float4.
+//   output       Y^T = Wo^T [O_0 .. O_{H-1}]^T: head hh's O^T result registers, split and
+//                exchanged through LDS, are the activation operand of MFMA hh;  lane (g, i)
+//                gets 4 consecutive output channels of row i, one float4.
 // K^T and V of every row tile stay in registers for the whole layer; Q^T is formed one
 // query tile at a time.  Rows past the centre's length are zeros in LDS, their keys are
 // masked to -inf and their outputs are never stored.
 //
-// On gfx950 the fp32 MFMA and the VALU do not execute concurrently (the co-execution counter
-// stays at zero and MFMA-busy + VALU-busy add up to the kernel time), so the softmax's VALU
-// instructions add directly to the MFMA time: every contraction accumulates in a single
-// chain (no partial sums to add up) and 1/Z uses the hardware reciprocal.
+// On gfx950 the matrix cores and the VALU do not execute concurrently (the co-execution
+// counter stays at zero and MFMA-busy + VALU-busy add up to the kernel time), so the
+// softmax's VALU instructions add directly to the MFMA time: every contraction accumulates
+// in a single chain (no partial sums to add up) and 1/Z uses the hardware reciprocal.
 #include "block_attn_fused.h"
 
 namespace nga {
@@ -39,28 +56,71 @@ namespace nga {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 __device__ inline f4 mfma4(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+__device__ inline f4 mfma16(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
-// Weights in operand order: for layer l, matrix m (q, k, v, o) and wavefront h, lane L holds
-// KS consecutive floats, element kk = W_m[k(kk, g)][16h + i] (lane L = 16g + i).
-__global__ void pack_weights_kernel(const float* __restrict__ w, int C, int H, int layers,
-                                    float* __restrict__ packed) {
-    const int KS = C / 4;
-    const int64_t total = (int64_t)layers * 4 * C * C;
-    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        int64_t rest = idx;
-        const int kk = (int)(rest % KS); rest /= KS;
-        const int lane = (int)(rest % 64); rest /= 64;
-        const int h = (int)(rest % H); rest /= H;
-        const int m = (int)(rest % 4); rest /= 4;
-        const int l = (int)rest;
+// Power-of-two exponent e with max |v| * 2^e in [2^13, 2^14); 0 for v == 0 and for a
+// non-finite maximum (the infinity then reaches the output as inf or NaN, as in fp32 math).
+// Split parts of values within 2^16 of the maximum then stay normal f16 numbers (the matrix
+// cores flush f16 subnormals), and the largest part stays far below the f16 maximum.
+__device__ inline int scale_exponent(float vmax) {
+    return vmax > 0.f && vmax <= 3.402823466e38f ? 13 - ilogbf(vmax) : 0;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// f16 (hi, lo) pair of v: hi is v rounded to f16, lo the remainder v - hi (exact in f32) rounded
+// to f16.  The empty asm pins v as one rounded f32 value: otherwise the compiler may fold the
+// product that made v into each conversion on its own (mixed-precision FMA with the unrounded
+// product), and at an f16 rounding tie the stored hi and the hi subtracted for lo then differ
+// by one f16 ulp.
+__device__ inline h2 split_f16(float v) {
+    asm("" : "+v"(v));
+    const _Float16 hi = (_Float16)v;
+    return h2{hi, (_Float16)(v - (float)hi)};
+}
+
+// Weights split into f16 (hi, lo) parts after scaling each matrix by 2^e (max |W| 2^e in
+// [2^13, 2^14)).  Operand of wavefront h, lane L = 16g + i, chunk u: 8 halves, the hi parts
+// of W[16u + 4g + e][16h + i] for e = 0..3 followed by their lo parts.  One work-group per
+// (layer, matrix); the exponent goes to expo[layer * 4 + m].
+__global__ void __launch_bounds__(256)
+pack_weights_kernel(const float* __restrict__ w, int C, int H, float* __restrict__ packed_f,
+                    int* __restrict__ expo) {
+    __shared__ float red[4];
+    const int lm = blockIdx.x;
+    const float* W = w + (size_t)lm * C * C;
+    float mx = 0.f;
+    for (int idx = threadIdx.x; idx < C * C; idx += 256) mx = fmaxf(mx, fabsf(W[idx]));
+    for (int d = 32; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int e = scale_exponent(mx);
+    if (threadIdx.x == 0) expo[lm] = e;
+    h8* packed = reinterpret_cast<h8*>(packed_f) + (size_t)lm * H * 64 * (C / 16);
+    const int total = H * 64 * (C / 16);
+    for (int idx = threadIdx.x; idx < total; idx += 256) {
+        const int u = idx % (C / 16);
+        const int lane = (idx / (C / 16)) % 64;
+        const int h = idx / (C / 16) / 64;
         const int g = lane >> 4, i = lane & 15;
-        const int k = 16 * (kk >> 2) + 4 * g + (kk & 3);
-        packed[idx] = w[(((int64_t)l * 4 + m) * C + k) * C + 16 * h + i];
+        h8 op;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const h2 p = split_f16(ldexpf(W[(size_t)(16 * u + 4 * g + q) * C + 16 * h + i], e));
+            op[q] = p[0];
+            op[4 + q] = p[1];
+        }
+        packed[idx] = op;
     }
 }
 
@@ -69,7 +129,8 @@ struct FusedArgs {
     const int32_t* order;
     const float* x;
     float* y;
-    const float* w;  // packed operand-order weights
+    const float* w;  // packed split weights
+    const int* expo;
     int n_centres;
     int64_t n_edges;
     int nnei_cap;
@@ -77,85 +138,92 @@ struct FusedArgs {
     uint32_t* status;
 };
 
-constexpr float kLog2e = 1.4426950408889634f;
-
-// Row stride (floats) of the LDS block: 4 floats of padding per row spread the float4 reads
-// of the 16 rows of a tile over the LDS banks.
+// LDS block row: 64 hi halves, 64 lo halves, 16 bytes of padding (272 bytes) -- or, between
+// layers, the row's C floats.
 template <int H>
 struct Lds {
     static constexpr int C = 16 * H;
-    static constexpr int XS = C + 4;
+    static constexpr int RB = 4 * C + 16;  // row bytes
 };
 
-// One layer of one centre whose block (NT row tiles) sits in sX.  K^T and V of every tile go
-// to registers; then for each query tile, Q^T is formed from the block, the scores, softmax
-// and values follow, the heads' outputs meet in LDS for the output projection, and the
-// result is stored to y (last layer) or written back over the block rows it came from
-// (earlier layers; those rows are no longer read in this layer).
+__device__ inline h8 dup_read(const unsigned char* p) {
+    const h4 v = *reinterpret_cast<const h4*>(p);
+    return h8{v[0], v[1], v[2], v[3], v[0], v[1], v[2], v[3]};
+}
+
 template <int H, int NT>
-__device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __restrict__ P,
-                                             const int64_t r0, const int n, const bool last,
-                                             float (*__restrict__ sX)[Lds<H>::XS],
-                                             f4 (*__restrict__ sO)[H][64],
-                                             float (*__restrict__ sWoh)[64], const int lane,
-                                             const int h) {
+__device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __restrict__ P,
+                                             const int layer, const int ex, const int64_t r0,
+                                             const int n, const bool last,
+                                             unsigned char* __restrict__ sX,
+                                             h8 (*__restrict__ sO)[H][64],
+                                             h8 (*__restrict__ sWoh)[64], float* red,
+                                             const int lane, const int h) {
     constexpr int C = 16 * H;
-    constexpr int KS = C / 4;
-    constexpr int MAT = H * 64 * KS;
+    constexpr int U = C / 16;
+    constexpr int RB = Lds<H>::RB;
+    constexpr int MAT = H * 64 * U;  // h8 per packed matrix
     const int g = lane >> 4;
     const int li = lane & 15;
-    const float c1 = kLog2e * 0.25f;  // log2(e) / sqrt(16)
+    const int eq = A.expo[4 * layer + 0], ek = A.expo[4 * layer + 1];
+    const int ev = A.expo[4 * layer + 2], eo = A.expo[4 * layer + 3];
+    // Scores carry 2^(2 ex + eq + ek); values and outputs 2^(ex + ev) and 2^(ex + ev + eo).
+    const float c1 = ldexpf(kLog2e * 0.25f, -(2 * ex + eq + ek));
 
-    float wq[KS], wk[KS], wv[KS];
+    h8 wq[U], wk[U], wv[U];
 #pragma unroll
-    for (int k4 = 0; k4 < KS / 4; ++k4) {
-        const f4 a = *reinterpret_cast<const f4*>(P + 0 * MAT + 4 * k4);
-        const f4 b = *reinterpret_cast<const f4*>(P + 1 * MAT + 4 * k4);
-        const f4 c = *reinterpret_cast<const f4*>(P + 2 * MAT + 4 * k4);
-        const f4 d = *reinterpret_cast<const f4*>(P + 3 * MAT + 4 * k4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wq[4 * k4 + i] = a[i];
-            wk[4 * k4 + i] = b[i];
-            wv[4 * k4 + i] = c[i];
-            sWoh[4 * k4 + i][lane] = d[i];
-        }
+    for (int u = 0; u < U; ++u) {
+        wq[u] = P[0 * MAT + u];
+        wk[u] = P[1 * MAT + u];
+        wv[u] = P[2 * MAT + u];
+        sWoh[u][lane] = P[3 * MAT + u];
     }
 
-    // Phase 1: K^T and V of every row tile, kept in registers.
     f4 kt[NT], vt[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        float xo[KS];
-#pragma unroll
-        for (int u = 0; u < C / 16; ++u) {
-            const f4 v = *reinterpret_cast<const f4*>(&sX[16 * t + li][16 * u + 4 * g]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) xo[4 * u + i] = v[i];
-        }
+        const unsigned char* row = sX + (16 * t + li) * RB;
         f4 k = {0.f, 0.f, 0.f, 0.f}, v = k;
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            k = mfma4(wk[kk], xo[kk], k);
-            v = mfma4(xo[kk], wv[kk], v);
+        for (int u = 0; u < U; ++u) {
+            const h8 xh = dup_read(row + 2 * (16 * u + 4 * g));
+            const h8 xl = dup_read(row + 2 * C + 2 * (16 * u + 4 * g));
+            k = mfma16(wk[u], xh, k);
+            k = mfma16(wk[u], xl, k);
+            v = mfma16(xh, wv[u], v);
+            v = mfma16(xl, wv[u], v);
         }
         kt[t] = k;
         vt[t] = v;
     }
+    // O is a convex combination of V rows, so max |V| over the centre bounds it: the scale
+    // that brings that bound to [2^13, 2^14) is shared by every head for the output projection.
+    float vmax = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vmax = fmaxf(vmax, fabsf(vt[t][r]));
+    for (int d = 32; d > 0; d >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, d, 64));
+    if (lane == 0) red[h] = vmax;
+    __syncthreads();
+    vmax = red[0];
+#pragma unroll
+    for (int w = 1; w < H; ++w) vmax = fmaxf(vmax, red[w]);
+    const int e_o = scale_exponent(vmax);
+    const float oscale = ldexpf(1.f, e_o);
+    const float yscale = ldexpf(1.f, -(ex + ev + e_o + eo));
 
-    // Phases 2 + 3, one query tile at a time.
     for (int qt = 0; qt < NT; ++qt) {
         f4 q = {0.f, 0.f, 0.f, 0.f};
         {
-            float xo[KS];
+            const unsigned char* row = sX + (16 * qt + li) * RB;
 #pragma unroll
-            for (int u = 0; u < C / 16; ++u) {
-                const f4 v = *reinterpret_cast<const f4*>(&sX[16 * qt + li][16 * u + 4 * g]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) xo[4 * u + i] = v[i];
+            for (int u = 0; u < U; ++u) {
+                const h8 xh = dup_read(row + 2 * (16 * u + 4 * g));
+                const h8 xl = dup_read(row + 2 * C + 2 * (16 * u + 4 * g));
+                q = mfma16(wq[u], xh, q);
+                q = mfma16(wq[u], xl, q);
             }
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) q = mfma4(wq[kk], xo[kk], q);
         }
         f4 s[NT];
 #pragma unroll
@@ -165,7 +233,6 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __
             for (int r = 0; r < 4; ++r) acc = mfma4(kt[t][r], q[r], acc);
             s[t] = acc;
         }
-        // Only the last key tile can hold keys past the row end.
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (16 * (NT - 1) + 4 * g + r >= n) s[NT - 1][r] = -INFINITY;
@@ -193,18 +260,29 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) osum = mfma4(vt[t][r], s[t][r], osum);
-        const f4 o = osum * __builtin_amdgcn_rcpf(z);
+        const f4 o = osum * (__builtin_amdgcn_rcpf(z) * oscale);
 
+        h8 os;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const h2 p = split_f16(o[r]);
+            os[r] = p[0];
+            os[4 + r] = p[1];
+        }
         const int buf = qt & 1;
-        sO[buf][h][lane] = o;
-        __syncthreads();  // every head's O of this tile is in LDS; every wave has read rows qt
+        sO[buf][h][lane] = os;
+        __syncthreads();
         f4 yv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int hh = 0; hh < H; ++hh) {
-            const f4 oo = sO[buf][hh][lane];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) yv = mfma4(sWoh[4 * hh + r][lane], oo[r], yv);
+            const h8 oo = sO[buf][hh][lane];
+            const h8 oh = h8{oo[0], oo[1], oo[2], oo[3], oo[0], oo[1], oo[2], oo[3]};
+            const h8 ol = h8{oo[4], oo[5], oo[6], oo[7], oo[4], oo[5], oo[6], oo[7]};
+            const h8 wo = sWoh[hh][lane];
+            yv = mfma16(wo, oh, yv);
+            yv = mfma16(wo, ol, yv);
         }
+        yv *= yscale;
         const int a = 16 * qt + li;
         if (last) {
             if (a < n) {
@@ -214,19 +292,60 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const float* __
             }
         } else {
             const f4 zero = {0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f4*>(&sX[a][16 * h + 4 * g]) = a < n ? yv : zero;
+            *reinterpret_cast<f4*>(sX + a * Lds<H>::RB + 4 * (16 * h + 4 * g)) = a < n ? yv : zero;
         }
     }
+}
+
+// Split the block's rows (held as floats in vals, PER float4 chunks per thread) into hi/lo
+// halves at the block's power-of-two scale; returns the exponent.
+template <int H, int PER>
+__device__ inline int split_block(f4 (&vals)[PER], int chunks, unsigned char* sX, float* red) {
+    constexpr int C = 16 * H;
+    constexpr int CH = C / 4;
+    constexpr int NTH = 64 * H;
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(vals[j][i]));
+    for (int d = 32; d > 0; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < H; ++w) mx = fmaxf(mx, red[w]);
+    const int e = scale_exponent(mx);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int idx = threadIdx.x + j * NTH;
+        if (idx >= chunks) continue;
+        const int a = idx / CH, c4 = idx % CH;
+        h4 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h2 p = split_f16(ldexpf(vals[j][i], e));
+            hi[i] = p[0];
+            lo[i] = p[1];
+        }
+        unsigned char* row = sX + a * Lds<H>::RB;
+        *reinterpret_cast<h4*>(row + 2 * (4 * c4)) = hi;
+        *reinterpret_cast<h4*>(row + 2 * C + 2 * (4 * c4)) = lo;
+    }
+    return e;
 }
 
 template <int H, int TMAX>
 __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
     constexpr int C = 16 * H;
-    constexpr int KS = C / 4;
+    constexpr int U = C / 16;
     constexpr int NTH = 64 * H;
-    __shared__ float sX[16 * TMAX][Lds<H>::XS];
-    __shared__ f4 sO[2][H][64];
-    __shared__ float sWo[H][KS][64];
+    constexpr int CH = C / 4;
+    constexpr int PER = (16 * TMAX * CH + NTH - 1) / NTH;
+    __shared__ __align__(16) unsigned char sX[16 * TMAX * Lds<H>::RB];
+    __shared__ h8 sO[2][H][64];
+    __shared__ h8 sWo[H][U][64];
+    __shared__ float red[H];
 
     const int lane = threadIdx.x & 63;
     const int h = threadIdx.x >> 6;
@@ -246,42 +365,32 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
             return;
         }
         const int nt = (n + 15) >> 4;
-
-        // Gather the block: rows a < n from x (through `order`), zeros up to the tile edge.
-        // All loads of a thread are issued before any LDS write.
-        {
-            constexpr int CH = C / 4;                          // float4 chunks per row
-            constexpr int PER = (16 * TMAX * CH + NTH - 1) / NTH;
-            f4 v[PER];
-            const int chunks = 16 * nt * CH;
+        const int chunks = 16 * nt * CH;
+        f4 v[PER];
 #pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int idx = threadIdx.x + j * NTH;
-                const int a = idx / CH, c4 = idx % CH;
-                v[j] = f4{0.f, 0.f, 0.f, 0.f};
-                if (idx < chunks && a < n) {
-                    const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
-                    if (row >= 0 && row < A.n_edges)
-                        v[j] = *reinterpret_cast<const f4*>(A.x + row * C + 4 * c4);
-                    else
-                        bad_index = true;
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int idx = threadIdx.x + j * NTH;
-                const int a = idx / CH, c4 = idx % CH;
-                if (idx < chunks) *reinterpret_cast<f4*>(&sX[a][4 * c4]) = v[j];
+        for (int j = 0; j < PER; ++j) {
+            const int idx = threadIdx.x + j * NTH;
+            const int a = idx / CH, c4 = idx % CH;
+            v[j] = f4{0.f, 0.f, 0.f, 0.f};
+            if (idx < chunks && a < n) {
+                const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+                if (row >= 0 && row < A.n_edges)
+                    v[j] = *reinterpret_cast<const f4*>(A.x + row * C + 4 * c4);
+                else
+                    bad_index = true;
             }
         }
+        int ex = split_block<H, PER>(v, chunks, sX, red);
         __syncthreads();
 
         for (int layer = 0; layer < A.layers; ++layer) {
-            const float* P = A.w + (size_t)layer * 4 * C * C + ((size_t)h * 64 + lane) * KS;
+            const h8* P = reinterpret_cast<const h8*>(A.w) + (size_t)layer * 4 * H * 64 * U +
+                          ((size_t)h * 64 + lane) * U;
             const bool last = layer == A.layers - 1;
-#define NGA_CASE(T)                                                                   \
-    case T:                                                                           \
-        if constexpr (T <= TMAX) centre_layer<H, T>(A, P, r0, n, last, sX, sO, sWo[h], lane, h); \
+#define NGA_CASE(T)                                                                            \
+    case T:                                                                                    \
+        if constexpr (T <= TMAX)                                                               \
+            centre_layer<H, T>(A, P, layer, ex, r0, n, last, sX, sO, sWo[h], red, lane, h);        \
         break;
             switch (nt) {
                 NGA_CASE(1) NGA_CASE(2) NGA_CASE(3) NGA_CASE(4) NGA_CASE(5) NGA_CASE(6)
@@ -289,7 +398,21 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
                 default: break;
             }
 #undef NGA_CASE
-            __syncthreads();  // the block (or this layer's rows) is complete before it is read
+            __syncthreads();
+            if (!last) {
+                // The rows now hold this layer's output as floats: re-split for the next.
+#pragma unroll
+                for (int j = 0; j < PER; ++j) {
+                    const int idx = threadIdx.x + j * NTH;
+                    const int a = idx / CH, c4 = idx % CH;
+                    v[j] = f4{0.f, 0.f, 0.f, 0.f};
+                    if (idx < chunks)
+                        v[j] = *reinterpret_cast<const f4*>(sX + a * Lds<H>::RB + 16 * c4);
+                }
+                __syncthreads();
+                ex = split_block<H, PER>(v, chunks, sX, red);
+                __syncthreads();
+            }
         }
     }
     if (bad_index) raise_bits(A.status, kBitIndex);
@@ -297,8 +420,6 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
 
 template <int H>
 int launch_h(int tmax, const FusedArgs& a, hipStream_t s) {
-    // One work-group per centre: the hardware keeps two resident per compute unit (LDS and
-    // registers) and starts the next as soon as one retires.
     dim3 grid((unsigned)a.n_centres), block(64 * H);
     if (tmax <= 4) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 4>), grid, block, 0, s, a);
     else if (tmax <= 8) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 8>), grid, block, 0, s, a);
@@ -320,18 +441,17 @@ const char* fused_name(int dtype, int32_t c, int32_t heads) {
     return "fused_f32_d16";
 }
 
-size_t fused_workspace_floats(int32_t c, int32_t layers) { return (size_t)layers * 4 * c * c; }
+size_t fused_workspace_floats(int32_t c, int32_t layers) { return (size_t)layers * 4 * c * c + 64 + 4 * layers; }
 
 int run_fused(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
               int64_t n_edges, int32_t nnei_cap, int32_t c, int32_t heads, int32_t layers,
               const void* weights, const void* x, void* y, void* packed, uint32_t* status,
               hipStream_t s) {
     (void)dtype;
-    const int64_t total = (int64_t)layers * 4 * c * c;
-    const unsigned pblocks = (unsigned)std::min<int64_t>((total + 255) / 256, 1024);
-    hipLaunchKernelGGL(pack_weights_kernel, dim3(pblocks), dim3(256), 0, s,
-                       static_cast<const float*>(weights), (int)c, (int)heads, (int)layers,
-                       static_cast<float*>(packed));
+    float* pk = static_cast<float*>(packed);
+    int* expo = reinterpret_cast<int*>(pk + (size_t)layers * 4 * c * c);
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)(layers * 4)), dim3(256), 0, s,
+                       static_cast<const float*>(weights), (int)c, (int)heads, pk, expo);
     int rc = last_launch_status();
     if (rc) return rc;
     FusedArgs a;
@@ -339,7 +459,8 @@ int run_fused(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n
     a.order = order;
     a.x = static_cast<const float*>(x);
     a.y = static_cast<float*>(y);
-    a.w = static_cast<const float*>(packed);
+    a.w = pk;
+    a.expo = expo;
     a.n_centres = (int)n_centres;
     a.n_edges = n_edges;
     a.nnei_cap = nnei_cap;

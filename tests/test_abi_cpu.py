@@ -127,5 +127,13 @@ def test_attention_workspace_and_variant_queries():
     assert lib.block_attn_workspace_bytes(9, 10, 8, 8, 2, 1) == 0
     g = lib.block_attn_workspace_bytes(L.NGA_F64, 1000, 40, 32, 4, 6)
     assert g >= 1000 * 32 * 8 * 5
-    assert nga.attn_variant(L.NGA_F64, 40, 32, 4).startswith(("generic", "fused"))
+    assert nga.attn_variant(L.NGA_F64, 40, 32, 4) == "mfma_f64"        # head width 8
+    assert nga.attn_variant(L.NGA_F64, 128, 128, 4) == "mfma_f64"      # head width 32, cap 128
+    assert nga.attn_variant(L.NGA_F64, 129, 128, 4) == "generic_f64"   # rows past 128
+    assert nga.attn_variant(L.NGA_F64, 40, 24, 3) == "mfma_f64"        # three heads of 8
+    assert nga.attn_variant(L.NGA_F64, 40, 20, 2) == "generic_f64"     # head width 10
+    assert nga.attn_variant(L.NGA_F32, 181, 64, 4) == "fused_f32_d16"
+    assert nga.attn_variant(L.NGA_F32, 192, 16, 1) == "fused_f32_d16"
+    assert nga.attn_variant(L.NGA_F32, 193, 64, 4) == "generic_f32"    # rows past 192
+    assert nga.attn_variant(L.NGA_F32, 60, 40, 5) == "generic_f32"     # head width 8
     assert nga.attn_variant(5, 40, 32, 4) == "unsupported"

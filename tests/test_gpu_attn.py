@@ -120,6 +120,71 @@ def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, see
     assert _normwise(y.astype(np.float64), ref) < TOL[dtype]
 
 
+def _per_centre_normwise(y, ref, rp):
+    worst = 0.0
+    for i in range(rp.shape[0] - 1):
+        if rp[i + 1] > rp[i]:
+            worst = max(worst, _normwise(y[rp[i]:rp[i + 1]], ref[rp[i]:rp[i + 1]]))
+    return worst
+
+
+def test_f32_split_rounding_ties(oracle_mod):
+    """fp32 projections on f16 matrix cores take each operand as two f16 parts (hi, lo).  Both
+    parts must come from one rounded fp32 value: a head-output element at an f16 rounding tie
+    otherwise gets its lo part from a differently rounded copy and lands one f16 ulp off.  The
+    first block is 41 seeded rows that hold such ties; the rest are 400 blocks of 30 to 48 rows,
+    over a million head-output elements."""
+    rp0 = W.random_rows(20, 64, 5, min_len=1)
+    x0 = W.make_features(int(rp0[-1]), 64, 6, np.float32)
+    wt = W.make_weights(1, 64, 7, np.float32)
+    blk = np.concatenate([x0[rp0[0]:rp0[1]], x0[100:]])[:41]
+    lens = np.random.default_rng(31).integers(30, 49, 400)
+    rp = np.concatenate([[0, 41], 41 + np.cumsum(lens)]).astype(np.int64)
+    x = np.concatenate([blk, W.make_features(int(lens.sum()), 64, 32, np.float32)])
+    y = _run(rp, x, wt, 4, 64)
+    ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), 4)
+    err = _per_centre_normwise(y.astype(np.float64), ref, rp)
+    print(f"worst per-centre normwise error {err:.3e}", flush=True)
+    assert err < TOL[np.float32]
+
+
+@pytest.mark.parametrize("heads,layers", [(4, 2), (2, 1), (1, 3)])
+def test_f32_per_centre_magnitudes(oracle_mod, heads, layers):
+    """Centres whose features differ in magnitude by up to 2^21 each keep fp32-class relative
+    accuracy against their own scale (the f16 split is scaled per centre and layer)."""
+    c = 16 * heads
+    rp = W.random_rows(60, 100, 41, min_len=1)
+    e = int(rp[-1])
+    x = W.make_features(e, c, 42, np.float32)
+    k = np.random.default_rng(43).integers(-20, 2, rp.shape[0] - 1)
+    for i in range(rp.shape[0] - 1):
+        x[rp[i]:rp[i + 1]] *= np.float32(2.0 ** k[i])
+    wt = W.make_weights(layers, c, 44, np.float32)
+    y = _run(rp, x, wt, heads, 100)
+    ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), heads)
+    err = _per_centre_normwise(y.astype(np.float64), ref, rp)
+    print(f"variant={nga.attn_variant(1, 100, c, heads)} worst per-centre error {err:.3e}",
+          flush=True)
+    assert err < TOL[np.float32]
+
+
+def test_f32_weight_magnitudes(oracle_mod):
+    """Weight matrices scaled far from 1 (2^-30 .. 2^30, with non-power-of-two factors) give
+    the same relative accuracy; the scales are paired so that the scores keep their size."""
+    rp = W.random_rows(40, 181, 51, min_len=1)
+    e = int(rp[-1])
+    x = W.make_features(e, 64, 52, np.float32)
+    wt = W.make_weights(2, 64, 53, np.float32)
+    for (l, m), s in zip([(0, 0), (0, 1), (0, 2), (0, 3), (1, 0), (1, 2), (1, 3)],
+                         [2.0 ** -30 * 3, 2.0 ** 28, 2.0 ** 30, 2.0 ** -30, 0.7, 2.0 ** -12, 5.0]):
+        wt[l, m] *= np.float32(s)
+    y = _run(rp, x, wt, 4, 181)
+    ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), 4)
+    err = _normwise(y.astype(np.float64), ref)
+    print(f"normwise error {err:.3e}", flush=True)
+    assert err < TOL[np.float32]
+
+
 @pytest.mark.parametrize("dtype,c,heads,cap", [(np.float64, 32, 4, 60), (np.float32, 64, 4, 181)])
 def test_order_gather_scatter(oracle_mod, dtype, c, heads, cap):
     rp = W.random_rows(30, cap, 77, min_len=1)
