@@ -9,46 +9,45 @@
 //
 // Work-group = H wavefronts, wavefront h owns head h (columns 16h .. 16h+15).
 //
-// Projections (Q, K, V from the block rows, Y from the heads' outputs) run on the f16 matrix
-// cores, v_mfma_f32_16x16x32_f16 with fp32 accumulation, on operands split into two f16
-// parts v = hi + lo after scaling by a power of two: the block's rows by 2^ex (one exponent
-// per centre and layer, max |x| 2^ex in [2^13, 2^14)), each weight matrix by its own 2^e,
-// the heads' outputs by 2^e_o (from the centre's max |V|, which bounds |O| because every O
-// row is a convex combination of V rows).  All four partial products go in: one MFMA takes
-// the weight's [hi, lo] parts against the activation's hi part (duplicated), a second one
-// against its lo part.  The pair of parts carries 22 significant bits; parts below the f16
-// normal range (the matrix cores flush f16 subnormals) lie under 2^-27 of the block's
-// maximum; every product is exact in the fp32 accumulator.  A 16-channel chunk then costs
-// two 16x16x32 f16 MFMAs (8 CU cycles at gfx950's dense f16 rate) where fp32 needs four
-// 16x16x4 MFMAs (32 CU cycles).  Scores S and the weighted values O stay on
-// v_mfma_f32_16x16x4_f32 with the projections' fp32 results as operands.
+// Every contraction -- the projections Q, K, V, Y and the scores S and weighted values O --
+// runs on the f16 matrix cores, v_mfma_f32_16x16x32_f16 with fp32 accumulation, on operands
+// split into two f16 parts v = hi + lo after scaling by a power of two:
+//   block rows      2^ex per centre and layer (max |x| 2^ex in [2^13, 2^14));
+//   weights         2^e per matrix;
+//   K               per head, from max |K| over the centre;
+//   Q               per query (one lane row), from max |Q| over the head's channels;
+//   V and O         per centre, from max |V| (every O row is a convex combination of V rows);
+//   P               2^13 (P <= 1 before scaling), folded into the exponent argument.
+// All four partial products go in: one MFMA takes [a_hi, a_lo] . [b_hi, b_lo], a second one
+// [a_hi, a_lo] . [b_lo, b_hi].  The pair of parts carries 21 or more significant bits; parts
+// below the f16 normal range (the matrix cores flush f16 subnormals) lie under 2^-27 of their
+// scale's maximum; every product is exact in the fp32 accumulator.  A 16-deep contraction
+// then costs two 16x16x32 f16 MFMAs (16 CU cycles at gfx950's dense f16 rate) where fp32
+// needs four 16x16x4 MFMAs (64 CU cycles).
 //
-// Operand / result layouts.  f32 16x16x4: A[i][k] from lane i + 16k, B[k][j] from lane
-// j + 16k.  f16 16x16x32: A[i][k] from lane i + 16(k/8), element k%8, and B[k][j] from lane
-// j + 16(k/8), element k%8.  Both write D[i][j] to lane j + 16(i/4), register i%4.  Every
-// result feeds the next contraction directly, by choosing the order in which each
-// contraction walks its k index:
-//   projections  Q^T = Wq_h^T X^T, K^T = Wk_h^T X^T, V = X Wv_h: MFMA u covers input
-//                channels 16u + 4g + e (lane group g, e = 0..3): the weight operand holds
-//                their hi parts in elements 0..3 and lo parts in 4..7, the activation
-//                operand a part of the same four channels twice;
-//   scores       S^T = K Q^T, k = head channel 4g + r: A = K^T result register r,
-//                B = Q^T result register r;  lane (g, i) then holds query i against keys
-//                4g+r of every key tile;
+// Operand / result layouts of the f16 16x16x32 MFMA: A[i][k] from lane i + 16(k/8),
+// element k%8; B[k][j] from lane j + 16(k/8), element k%8; D[i][j] in lane j + 16(i/4),
+// register i%4.  With k = 8g + e standing for channel (or key) 4g + e%4, hi part for e < 4
+// and lo part for e >= 4, each result is already the next contraction's operand:
+//   projections  Q^T = Wq_h^T X^T, K^T = Wk_h^T X^T (A = weights, B = block rows),
+//                V = X Wv_h (A = block rows, B = weights), 16-channel chunk u per MFMA pair:
+//                lane (g, i) holds Q, K of row i, channels 4g .. 4g+3, and V of rows
+//                4g .. 4g+3, channel i;
+//   scores       S^T = K Q^T: A = K of key tile t, B = Q of the query tile, both split in
+//                place;  lane (g, i) then holds query i against keys 4g .. 4g+3 of tile t;
 //   softmax      row max / sum over a lane's registers and the 4 lane groups (2 shuffles);
-//   values       O^T = V^T P^T, k = key 16kt + 4g + r: A = V result register r,
-//                B = P register r;
-//   output       Y^T = Wo^T [O_0 .. O_{H-1}]^T: head hh's O^T result registers, split and
-//                exchanged through LDS, are the activation operand of MFMA hh;  lane (g, i)
-//                gets 4 consecutive output channels of row i, one float4.
-// K^T and V of every row tile stay in registers for the whole layer; Q^T is formed one
+//   values       O^T = V^T P^T: A = V of key tile t, B = P of tile t, split in place;
+//   output       Y^T = Wo^T [O_0 .. O_{H-1}]^T: head hh's O^T (channels 4g .. 4g+3 of query
+//                i in lane (g, i)), split and exchanged through LDS, is the B operand of the
+//                MFMA pair hh;  lane (g, i) gets 4 consecutive output channels of row i.
+// K and V of every key tile stay in registers, split, for the whole layer; Q is formed one
 // query tile at a time.  Rows past the centre's length are zeros in LDS, their keys are
 // masked to -inf and their outputs are never stored.
 //
 // On gfx950 the matrix cores and the VALU do not execute concurrently (the co-execution
-// counter stays at zero and MFMA-busy + VALU-busy add up to the kernel time), so the
-// softmax's VALU instructions add directly to the MFMA time: every contraction accumulates
-// in a single chain (no partial sums to add up) and 1/Z uses the hardware reciprocal.
+// counter stays at zero and MFMA-busy + VALU-busy add up to the kernel time), so VALU work
+// adds directly to the MFMA time: contractions accumulate in a single chain, 1/Z uses the
+// hardware reciprocal, and the splits use packed conversions and mixed-precision FMAs.
 #include "block_attn_fused.h"
 
 namespace nga {
@@ -146,6 +145,32 @@ struct Lds {
     static constexpr int RB = 4 * C + 16;  // row bytes
 };
 
+// [hi, lo] f16 operand of the four values v * 2^e.  hi: the values rounded toward zero to
+// f16 by the packed conversion; lo: v - hi (exact in fp32) rounded to f16.  Any hi works as
+// long as lo is taken from that same hi.  The multiply by an opaque 1.0 lets the compiler form
+// each lo half with one mixed-precision FMA reading fp32 v and one f16 half of hi.
+__device__ inline h8 split4(f4 v, int e) {
+    float one = 1.0f;
+    asm("" : "+v"(one));
+    f4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = ldexpf(v[i], e);
+        asm("" : "+v"(w[i]));
+    }
+    const h2 h01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
+    const h2 h23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(w[2], w[3]));
+    h8 r;
+    r[0] = h01[0]; r[1] = h01[1]; r[2] = h23[0]; r[3] = h23[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[4 + i] = (_Float16)__builtin_fmaf(w[i], one, -(float)r[i]);
+    return r;
+}
+
+__device__ inline h8 swap_halves(h8 v) {
+    return __builtin_shufflevector(v, v, 4, 5, 6, 7, 0, 1, 2, 3);
+}
+
 __device__ inline h8 dup_read(const unsigned char* p) {
     const h4 v = *reinterpret_cast<const h4*>(p);
     return h8{v[0], v[1], v[2], v[3], v[0], v[1], v[2], v[3]};
@@ -167,8 +192,8 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
     const int li = lane & 15;
     const int eq = A.expo[4 * layer + 0], ek = A.expo[4 * layer + 1];
     const int ev = A.expo[4 * layer + 2], eo = A.expo[4 * layer + 3];
-    // Scores carry 2^(2 ex + eq + ek); values and outputs 2^(ex + ev) and 2^(ex + ev + eo).
-    const float c1 = ldexpf(kLog2e * 0.25f, -(2 * ex + eq + ek));
+    // K and Q leave the projections scaled by 2^(ex + ek) and 2^(ex + eq); values and outputs
+    // by 2^(ex + ev) and 2^(ex + ev + eo).
 
     h8 wq[U], wk[U], wv[U];
 #pragma unroll
@@ -196,6 +221,20 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
         kt[t] = k;
         vt[t] = v;
     }
+    // K rescaled per head (max |K| over the centre to [2^13, 2^14)) and split: lane (i, g) of
+    // key tile t then holds [K_hi, K_lo] of key 16t + i, channels 4g .. 4g+3, which is the A
+    // operand of S^T = K Q^T on the f16 cores.
+    float kmax = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kmax = fmaxf(kmax, fabsf(kt[t][r]));
+    for (int d = 32; d > 0; d >>= 1) kmax = fmaxf(kmax, __shfl_xor(kmax, d, 64));
+    const int e_k = scale_exponent(kmax);
+    h8 ka[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ka[t] = split4(kt[t], e_k);
+
     // O is a convex combination of V rows, so max |V| over the centre bounds it: the scale
     // that brings that bound to [2^13, 2^14) is shared by every head for the output projection.
     float vmax = 0.f;
@@ -210,8 +249,12 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
 #pragma unroll
     for (int w = 1; w < H; ++w) vmax = fmaxf(vmax, red[w]);
     const int e_o = scale_exponent(vmax);
-    const float oscale = ldexpf(1.f, e_o);
     const float yscale = ldexpf(1.f, -(ex + ev + e_o + eo));
+    // V at that scale, split: lane (i, g) of key tile t holds [V_hi, V_lo] of keys
+    // 16t + 4g .. 16t + 4g + 3, channel i -- the A operand of O^T = V^T P^T.
+    h8 va[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) va[t] = split4(vt[t], e_o);
 
     for (int qt = 0; qt < NT; ++qt) {
         f4 q = {0.f, 0.f, 0.f, 0.f};
@@ -225,13 +268,21 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
                 q = mfma16(wq[u], xl, q);
             }
         }
+        // Q rescaled per query (lane (i, g) holds channels 4g .. 4g+3 of query i; the scale
+        // is shared by the 4 lane groups) and split: the B operand of S^T = K Q^T.
+        float qm = fmaxf(fmaxf(fabsf(q[0]), fabsf(q[1])), fmaxf(fabsf(q[2]), fabsf(q[3])));
+        qm = fmaxf(qm, __shfl_xor(qm, 16, 64));
+        qm = fmaxf(qm, __shfl_xor(qm, 32, 64));
+        const int e_q = scale_exponent(qm);
+        const h8 qa = split4(q, e_q);
+        const h8 qb = swap_halves(qa);
+        const float c1 = ldexpf(kLog2e * 0.25f, -(2 * ex + eq + ek + e_k + e_q));
         f4 s[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc = mfma4(kt[t][r], q[r], acc);
-            s[t] = acc;
+            // [K_hi, K_lo] . [Q_hi, Q_lo] + [K_hi, K_lo] . [Q_lo, Q_hi]
+            f4 acc = mfma16(ka[t], qa, f4{0.f, 0.f, 0.f, 0.f});
+            s[t] = mfma16(ka[t], qb, acc);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -243,7 +294,8 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
             for (int r = 0; r < 4; ++r) m = fmaxf(m, s[t][r]);
         m = fmaxf(m, __shfl_xor(m, 16, 64));
         m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const float mc = m * c1;
+        // P scaled by 2^13 (max P = 2^13) so that its split parts stay normal f16 numbers.
+        const float mc = m * c1 - 13.f;
         float z = 0.f;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -257,10 +309,13 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
         z += __shfl_xor(z, 32, 64);
         f4 osum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) osum = mfma4(vt[t][r], s[t][r], osum);
-        const f4 o = osum * (__builtin_amdgcn_rcpf(z) * oscale);
+        for (int t = 0; t < NT; ++t) {
+            // [V_hi, V_lo] . [P_hi, P_lo] + [V_hi, V_lo] . [P_lo, P_hi]
+            const h8 pa = split4(s[t], 0);
+            osum = mfma16(va[t], pa, osum);
+            osum = mfma16(va[t], swap_halves(pa), osum);
+        }
+        const f4 o = osum * __builtin_amdgcn_rcpf(z);
 
         h8 os;
 #pragma unroll
