@@ -145,19 +145,15 @@ struct Lds {
     static constexpr int RB = 4 * C + 16;  // row bytes
 };
 
-// [hi, lo] f16 operand of the four values v * 2^e.  hi: the values rounded toward zero to
-// f16 by the packed conversion; lo: v - hi (exact in fp32) rounded to f16.  Any hi works as
-// long as lo is taken from that same hi.  The multiply by an opaque 1.0 lets the compiler form
-// each lo half with one mixed-precision FMA reading fp32 v and one f16 half of hi.
-__device__ inline h8 split4(f4 v, int e) {
+// [hi, lo] f16 operand of the four values w.  hi: the values rounded toward zero to f16 by
+// the packed conversion; lo: w - hi (exact in fp32) rounded to f16.  Any hi works as long as
+// lo is taken from that same hi.  The multiply by an opaque 1.0 lets the compiler form each lo
+// half with one mixed-precision FMA reading fp32 w and one f16 half of hi.
+__device__ inline h8 split4_unscaled(f4 w) {
     float one = 1.0f;
     asm("" : "+v"(one));
-    f4 w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w[i] = ldexpf(v[i], e);
-        asm("" : "+v"(w[i]));
-    }
+    for (int i = 0; i < 4; ++i) asm("" : "+v"(w[i]));
     const h2 h01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(w[0], w[1]));
     const h2 h23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(w[2], w[3]));
     h8 r;
@@ -165,6 +161,14 @@ __device__ inline h8 split4(f4 v, int e) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[4 + i] = (_Float16)__builtin_fmaf(w[i], one, -(float)r[i]);
     return r;
+}
+
+// The same for the four values v * 2^e.
+__device__ inline h8 split4(f4 v, int e) {
+    f4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = ldexpf(v[i], e);
+    return split4_unscaled(w);
 }
 
 __device__ inline h8 swap_halves(h8 v) {
@@ -311,7 +315,7 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             // [V_hi, V_lo] . [P_hi, P_lo] + [V_hi, V_lo] . [P_lo, P_hi]
-            const h8 pa = split4(s[t], 0);
+            const h8 pa = split4_unscaled(s[t]);
             osum = mfma16(va[t], pa, osum);
             osum = mfma16(va[t], swap_halves(pa), osum);
         }
