@@ -43,6 +43,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--pair-axis", action="store_true",
+                    help="also time pair_attn_forward (the ragged pair-axis route) on the same "
+                         "inputs, after the timed steps, and report it beside the block-dense "
+                         "forward")
+    ap.add_argument("--pair-steps", type=int, default=2)
+    ap.add_argument("--pair-chunk", type=int, default=1 << 26,
+                    help="pairs per chunk of the pair-axis route")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter scaling)")
@@ -98,6 +105,45 @@ def cpu_baseline(w, pos, box, rp, x, wt, target_s):
     return {"value": m / t, "unit": "atoms/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{m} random centres of {n}: brute-force rows over all atoms and images, "
                       f"then naive attention through {w.layers} layer(s); {t:.1f} s wall"}
+
+
+def time_pair_axis(nga, torch, dev, stream, row_ptr, x, wt, w, rp, steps, chunk, y_block,
+                   attn_ms):
+    """The ragged pair-axis route on the same CSR and inputs: one untimed pass, then `steps`
+    timed passes (HIP events on the current stream; each pass synchronises once itself to
+    plan its chunks, so the events bracket exactly one forward)."""
+    counts = np.diff(rp)
+    pairs = int(np.sum(counts.astype(np.int64) ** 2))
+    # No chunk larger than the whole pair axis (the per-pair buffers are sized by the chunk).
+    chunk = int(min(chunk, max(pairs, int(np.max(counts.astype(np.int64) ** 2)), 1)))
+    n_chunks, acc = 0, 0
+    for c2 in (counts.astype(np.int64) ** 2):
+        if acc + c2 > chunk:
+            n_chunks, acc = n_chunks + 1, 0
+        acc += c2
+    n_chunks += 1 if acc > 0 else 0
+    ws = nga.Workspace(dev, nga.pair_attn_workspace_bytes(
+        nga.NGA_F64 if w.dtype == "f64" else nga.NGA_F32, rp.shape[0] - 1, x.shape[0], w.c,
+        w.heads, w.layers, chunk))
+    yp = torch.empty_like(x)
+    nga.pair_attn_forward(row_ptr, x, wt, w.heads, pair_chunk=chunk, y=yp, ws=ws)
+    nga.check_status(ws, "pair_attn_forward")
+    times = []
+    for _ in range(steps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        nga.pair_attn_forward(row_ptr, x, wt, w.heads, pair_chunk=chunk, y=yp, ws=ws)
+        ev1.record(stream)
+        torch.cuda.synchronize(dev)
+        times.append(ev0.elapsed_time(ev1))
+    nga.check_status(ws, "pair_attn_forward")
+    diff = float((yp - y_block).abs().max() / y_block.abs().max())
+    ms = float(np.mean(times))
+    es = 8 if w.dtype == "f64" else 4
+    return {"ms_per_forward": ms, "pairs": pairs, "pair_chunk": chunk, "chunks": n_chunks,
+            "pair_tensor_bytes": pairs * w.c * es,
+            "workspace_bytes": ws.nbytes, "vs_block_attn_forward": ms / attn_ms,
+            "normwise_diff_vs_block": diff, "steps": steps}
 
 
 def main():
@@ -183,6 +229,11 @@ def main():
                       ev[2].elapsed_time(ev[3])] for ev in events])
     nl_ms, csr_ms, attn_ms = (float(v) for v in part.mean(axis=0))
 
+    pair_rec = None
+    if args.pair_axis:
+        pair_rec = time_pair_axis(nga, torch, dev, stream, csr_out["row_ptr"][: n + 1], x, wt, w,
+                                  rp, args.pair_steps, args.pair_chunk, y, attn_ms)
+
     if args.copy_calib_mib > 0:
         nel = args.copy_calib_mib * (1 << 20) // 4
         src = torch.ones(nel, dtype=torch.float32, device=dev)
@@ -231,6 +282,8 @@ def main():
         "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
                    "frac": nl_gbs / PEAK_HBM_GBS},
     }
+    if pair_rec is not None:
+        rec["pair_axis"] = pair_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, pos_np, box, rp, x_np, wt_np, args.cpu_seconds)
     else:

@@ -7,6 +7,8 @@
  *   nl_build            O(N) cell-list neighbour rows under periodic boundaries
  *   edge_csr            those rows as a destination CSR with image shifts
  *   block_attn_forward  block-dense multi-head attention through the CSR
+ *   pair_attn_forward   the same attention by the ragged pair-axis route
+ *                       (a measured comparator)
  *
  * Sources (web pages, cited by title and section):
  *   [P1] deepmd-kit issue "perf: DPA4 .pt2 LAMMPS (C++ AOTI) inference 3-6x
@@ -21,7 +23,8 @@
  *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
  *     work on that stream and returns; nothing synchronises except where a
  *     host readback is asked for explicitly (edge_csr's h_n_edges,
- *     nga_sync_status).  No call allocates or frees memory: the caller owns
+ *     nga_sync_status) and in the pair-axis comparator, whose declaration
+ *     says so.  No call allocates or frees device memory: the caller owns
  *     every buffer, including the workspace, sized by the *_workspace_bytes
  *     queries (pure host arithmetic).  Keeping the data on the GPU from
  *     positions to outputs, with one optional readback, is what [P1]
@@ -185,6 +188,48 @@ int block_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
                        int64_t n_centres, int64_t n_edges, int32_t nnei_cap, int32_t c,
                        int32_t n_heads, int32_t n_layers, const void* weights, const void* x,
                        void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Ragged pair-axis attention (measured comparator)                          */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes pair_attn_forward needs for these shapes and chunks of at
+ * most pair_chunk pairs; 0 if the arguments are invalid. */
+size_t pair_attn_workspace_bytes(int dtype, int64_t n_centres, int64_t n_edges, int32_t c,
+                                 int32_t n_heads, int32_t n_layers, int64_t pair_chunk);
+
+/*
+ * The same y as block_attn_forward, computed by the ragged pair-axis route
+ * that the block-dense path replaces ([P2] "Root cause": enumerate the
+ * P = sum_i n_i^2 centre pairs, materialise (P, channels) intermediates, and
+ * run segment softmax + index_add over them).  Per layer:
+ *   qkv = x [Wq | Wk | Wv] for every edge;
+ *   for every pair p = (query edge a, key edge b) of one centre:
+ *     prod[p][t] = q_a[t] k_b[t]                      (P x c, materialised)
+ *     s[p][h]    = sum over head h's channels of prod[p] / sqrt(d)
+ *     m[a][h]    = max over a's pairs of s             (atomic scatter-max)
+ *     e[p][h]    = exp(s[p][h] - m[a][h]);  z[a][h] += e[p][h]  (atomic)
+ *     w[p][h]    = e[p][h] / z[a][h]
+ *     wv[p][t]   = w[p][h(t)] v_b[t]                   (P x c, materialised)
+ *     o[a][t]   += wv[p][t]                            (index_add, atomic)
+ *   y = o Wo.
+ * It exists to be measured beside block_attn_forward; its results agree with
+ * it to the floating-point tolerance (atomic accumulation order varies).
+ *
+ * The pairs are taken in chunks of whole centres holding at most pair_chunk
+ * pairs each, so the per-pair tensors need pair_chunk * (c + n_heads)
+ * elements plus 8 bytes per pair instead of P * c.
+ *
+ * Arguments as block_attn_forward, plus pair_chunk >= the largest n_i^2
+ * (NGA_EINVAL otherwise) and <= 2^31 - 1.  Unlike the other calls this one
+ * synchronises `stream` once, to read row_ptr back and plan the chunks on
+ * the host (host memory for n_centres + 1 offsets); everything else is
+ * enqueued.  Device-detected: NGA_EINDEX (order out of range).
+ */
+int pair_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
+                      int64_t n_centres, int64_t n_edges, int32_t c, int32_t n_heads,
+                      int32_t n_layers, const void* weights, const void* x, void* y,
+                      int64_t pair_chunk, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Status                                                                    */

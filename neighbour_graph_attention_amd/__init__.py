@@ -4,7 +4,9 @@ Python face of libnga.so, the C-ABI library declared in include/nga.h:
 
 * ``nl_build``: O(N) cell-list neighbour rows under periodic boundaries;
 * ``edge_csr``: those rows as a destination CSR with image shifts;
-* ``block_attn_forward``: block-dense multi-head attention through the CSR.
+* ``block_attn_forward``: block-dense multi-head attention through the CSR;
+* ``pair_attn_forward``: the same attention by the ragged pair-axis route, a
+  measured comparator.
 
 Importing the package loads the library and fails loudly if it has not been
 built (``neighbour_graph_attention_amd._build.build()``).
@@ -24,6 +26,8 @@ from ._lib import (  # noqa: F401
     load,
     nl_build,
     nl_build_workspace_bytes,
+    pair_attn_forward,
+    pair_attn_workspace_bytes,
     strerror,
     sync_status,
 )

@@ -23,7 +23,7 @@ ROW_CAP = 512
 
 EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "edge_csr",
            "block_attn_workspace_bytes", "block_attn_forward", "nga_sync_status", "nga_strerror",
-           "nga_attn_variant")
+           "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward")
 
 
 class NGAError(RuntimeError):
@@ -58,6 +58,11 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward.restype = ctypes.c_int
     lib.block_attn_forward.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp,
                                        vp, vp, sz, vp]
+    lib.pair_attn_workspace_bytes.restype = sz
+    lib.pair_attn_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32, i32, i32, i64]
+    lib.pair_attn_forward.restype = ctypes.c_int
+    lib.pair_attn_forward.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, vp, vp, vp,
+                                      i64, vp, sz, vp]
     lib.nga_sync_status.restype = ctypes.c_int
     lib.nga_sync_status.argtypes = [vp, vp]
     lib.nga_strerror.restype = ctypes.c_char_p
@@ -275,4 +280,46 @@ def block_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Te
                                 int(n_heads), int(layers), _ptr(weights), _ptr(x), _ptr(y),
                                 ws.ptr(), ws.nbytes, _stream(dev))
     _check(rc, "block_attn_forward")
+    return y
+
+
+DEFAULT_PAIR_CHUNK = 1 << 24
+
+
+def pair_attn_workspace_bytes(dtype: int, n_centres: int, n_edges: int, c: int, n_heads: int,
+                              n_layers: int, pair_chunk: int = DEFAULT_PAIR_CHUNK) -> int:
+    return int(load().pair_attn_workspace_bytes(dtype, n_centres, n_edges, c, n_heads, n_layers,
+                                                int(pair_chunk)))
+
+
+def pair_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Tensor,
+                      n_heads: int, *, order: torch.Tensor | None = None,
+                      pair_chunk: int = DEFAULT_PAIR_CHUNK, y: torch.Tensor | None = None,
+                      ws: Workspace | None = None):
+    """The same attention by the ragged pair-axis route (chunks of at most pair_chunk pairs);
+    returns y [E][c].  Synchronises the current stream once (chunk planning)."""
+    lib = load()
+    dev = x.device
+    e, c = x.shape
+    dt = _attn_dtype(x)
+    n_centres = row_ptr.shape[0] - 1
+    _need(row_ptr, "row_ptr", torch.int64, (n_centres + 1,), dev)
+    if weights.dim() != 4:
+        raise ValueError("weights must be [layers][4][c][c]")
+    layers = weights.shape[0]
+    _need(weights, "weights", x.dtype, (layers, 4, c, c), dev)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if order is not None:
+        if order.dim() != 1 or order.dtype != torch.int32 or order.device != dev or \
+                not order.is_contiguous():
+            raise ValueError("order must be a contiguous int32 vector on the device")
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, (e, c), dev)
+    ws = _ws(ws, dev, pair_attn_workspace_bytes(dt, n_centres, e, c, n_heads, layers, pair_chunk))
+    rc = lib.pair_attn_forward(dt, _ptr(row_ptr), _ptr(order), n_centres, e, c, int(n_heads),
+                               int(layers), _ptr(weights), _ptr(x), _ptr(y), int(pair_chunk),
+                               ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "pair_attn_forward")
     return y

@@ -122,6 +122,37 @@ def test_block_attn_rejects_bad_arguments():
     assert call(ne=0) == L.NGA_OK
 
 
+def test_pair_attn_rejects_bad_arguments():
+    lib = nga.load()
+    big = 1 << 40
+
+    def call(dt=L.NGA_F32, nc=4, ne=40, c=16, h=4, layers=1, rp=FAKE, w=FAKE,
+             x=0x100000, y=0x900000, chunk=1024, ws=FAKE, wsb=big):
+        return lib.pair_attn_forward(dt, rp, None, nc, ne, c, h, layers, w,
+                                     ctypes.c_void_p(x), ctypes.c_void_p(y), chunk, ws, wsb, None)
+
+    assert call(dt=7) == L.NGA_EDTYPE
+    assert call(c=18, h=4) == L.NGA_EINVAL           # c not divisible by heads
+    assert call(h=0) == L.NGA_EINVAL
+    assert call(layers=0) == L.NGA_EINVAL
+    assert call(chunk=0) == L.NGA_EINVAL
+    assert call(chunk=1 << 31) == L.NGA_EINVAL       # chunk above 2^31 - 1 pairs
+    assert call(ne=1 << 31) == L.NGA_EINVAL          # slots are int32
+    assert call(rp=None) == L.NGA_EINVAL
+    assert call(w=None) == L.NGA_EINVAL
+    assert call(y=0x100000 + 8) == L.NGA_EINVAL      # x and y overlap
+    assert call(ws=None) == L.NGA_EWORKSPACE
+    assert call(wsb=4) == L.NGA_EWORKSPACE
+    assert call(nc=0) == L.NGA_OK                    # nothing to do
+    assert call(ne=0) == L.NGA_OK
+    # workspace: per-edge buffers plus the chunk's per-pair buffers
+    b1 = lib.pair_attn_workspace_bytes(L.NGA_F32, 100, 1000, 64, 4, 1, 1 << 10)
+    b2 = lib.pair_attn_workspace_bytes(L.NGA_F32, 100, 1000, 64, 4, 1, 1 << 20)
+    assert b2 - b1 >= ((1 << 20) - (1 << 10)) * (8 + 4 * (64 + 4))
+    assert lib.pair_attn_workspace_bytes(L.NGA_F64, 100, 1000, 64, 4, 1, 1 << 10) > b1
+    assert lib.pair_attn_workspace_bytes(L.NGA_F32, 100, 1000, 64, 4, 1, 0) == 0
+
+
 def test_attention_workspace_and_variant_queries():
     lib = nga.load()
     assert lib.block_attn_workspace_bytes(9, 10, 8, 8, 2, 1) == 0
