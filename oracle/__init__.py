@@ -59,6 +59,8 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp]
+    lib.orc_attn_smooth.restype = ctypes.c_int
+    lib.orc_attn_smooth.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.orc_attn_naive_centres.restype = ctypes.c_int
     lib.orc_attn_naive_centres.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -154,6 +156,23 @@ def attn_naive(row_ptr, x, w, heads: int, order=None):
                             w.shape[0], _ptr(w), _ptr(x), _ptr(y))
     if rc != 0:
         raise ValueError("oracle attn_naive failed")
+    return y
+
+
+def attn_smooth(row_ptr, x, w, heads: int, log_dtilde, order=None):
+    """Smooth attention: stacked layers with each segment's softmax rescaled by
+    sum_j e_j / D~.  log_dtilde: ln D~ as [L][E][heads], keyed by the query edge's row."""
+    lib = _load()
+    row_ptr, order, x, w = _attn_args(row_ptr, order, x, w)
+    e, c = x.shape
+    ldt = _f64(log_dtilde)
+    if ldt.shape != (w.shape[0], e, heads):
+        raise ValueError("log_dtilde must be [layers][E][heads]")
+    y = np.zeros_like(x)
+    rc = lib.orc_attn_smooth(_ptr(row_ptr), _ptr(order), row_ptr.shape[0] - 1, e, c, heads,
+                             w.shape[0], _ptr(w), _ptr(x), _ptr(ldt), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle attn_smooth failed")
     return y
 
 

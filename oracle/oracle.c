@@ -236,9 +236,18 @@ static void orc_matmul(const double* x, int64_t n, int32_t c, const double* W, d
  *   Y = o Wo
  * W points at the layer's [4][c][c] weights (q, k, v, o).  scratch holds
  * 4*n*c + n doubles.
+ *
+ * Smooth attention ([P2] "Graph-native alternatives": the occupancy-modified
+ * weights are w_j = softmax_j * (sum_j e_j / D~), a per-segment scalar
+ * rescale of the vanilla softmax, with D~ computed outside the attention):
+ * when log_dt is not NULL it holds ln D~ for each block row a and head h at
+ * log_dt[a*heads + h], e_j = exp(s_j) is the unnormalised weight of the
+ * segment (query row a, head h), and
+ *     o_a[h cols] = (vanilla o_a[h cols]) * (sum_j e_j / D~),
+ * with sum_j e_j = exp(m) * Z, the factor evaluated as exp(m + ln Z - ln D~).
  */
 static void orc_layer_block(const double* X, int64_t n, int32_t c, int32_t heads,
-                            const double* W, double* Y, double* scratch)
+                            const double* W, const double* log_dt, double* Y, double* scratch)
 {
     const int64_t cc = (int64_t)c * c;
     const int32_t d = c / heads;
@@ -266,10 +275,11 @@ static void orc_layer_block(const double* X, int64_t n, int32_t c, int32_t heads
                 s[b] = exp(s[b] - m);
                 z += s[b];
             }
+            const double factor = log_dt ? exp(m + log(z) - log_dt[a * heads + h]) : 1.0;
             for (int32_t t = 0; t < d; ++t) {
                 double acc = 0.0;
                 for (int64_t b = 0; b < n; ++b) acc += s[b] * v[b * c + c0 + t];
-                o[a * c + c0 + t] = acc / z;
+                o[a * c + c0 + t] = acc / z * factor;
             }
         }
     }
@@ -297,12 +307,13 @@ static int64_t orc_max_row(const int64_t* row_ptr, int64_t n_centres)
  * layer gathers every centre's block through the destination CSR
  * (row_ptr, optional order permutation), runs orc_layer_block and scatters
  * the rows back; then x <- y for the next layer.
- * x, y: [n_edges][c] fp64; w: [layers][4][c][c] fp64.  Returns 0, or -1 on
- * bad arguments / out of memory.
+ * x, y: [n_edges][c] fp64; w: [layers][4][c][c] fp64; log_dt: NULL, or
+ * ln D~ as [layers][n_edges][heads] keyed by the query edge's row of x.
+ * Returns 0, or -1 on bad arguments / out of memory.
  */
-int orc_attn_naive(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
-                   int64_t n_edges, int32_t c, int32_t heads, int32_t layers,
-                   const double* w, const double* x, double* y)
+static int orc_attn_layers(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                           int64_t n_edges, int32_t c, int32_t heads, int32_t layers,
+                           const double* w, const double* x, const double* log_dt, double* y)
 {
     if (c < 1 || heads < 1 || c % heads != 0 || layers < 1) return -1;
     const int64_t nmax = orc_max_row(row_ptr, n_centres);
@@ -317,26 +328,49 @@ int orc_attn_naive(const int64_t* row_ptr, const int32_t* order, int64_t n_centr
             double* Xb = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
             double* Yb = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
             double* sc = (double*)malloc(((size_t)4 * (nmax + 1) * c + nmax + 1) * sizeof(double));
-            if (!Xb || !Yb || !sc) failed = 1;
+            double* Lb = (double*)malloc((size_t)(nmax + 1) * heads * sizeof(double));
+            if (!Xb || !Yb || !sc || !Lb) failed = 1;
 #pragma omp for schedule(dynamic, 8)
             for (int64_t i = 0; i < n_centres; ++i) {
                 if (failed) continue;
                 int64_t n = row_ptr[i + 1] - row_ptr[i];
                 if (n <= 0) continue;
-                for (int64_t a = 0; a < n; ++a)
-                    memcpy(Xb + a * c, cur + orc_edge_of(row_ptr, order, i, a) * c,
-                           (size_t)c * sizeof(double));
-                orc_layer_block(Xb, n, c, heads, W, Yb, sc);
+                for (int64_t a = 0; a < n; ++a) {
+                    const int64_t e = orc_edge_of(row_ptr, order, i, a);
+                    memcpy(Xb + a * c, cur + e * c, (size_t)c * sizeof(double));
+                    if (log_dt)
+                        memcpy(Lb + a * heads, log_dt + ((size_t)l * n_edges + e) * heads,
+                               (size_t)heads * sizeof(double));
+                }
+                orc_layer_block(Xb, n, c, heads, W, log_dt ? Lb : NULL, Yb, sc);
                 for (int64_t a = 0; a < n; ++a)
                     memcpy(y + orc_edge_of(row_ptr, order, i, a) * c, Yb + a * c,
                            (size_t)c * sizeof(double));
             }
-            free(Xb); free(Yb); free(sc);
+            free(Xb); free(Yb); free(sc); free(Lb);
         }
         if (l + 1 < layers) memcpy(cur, y, (size_t)n_edges * c * sizeof(double));
     }
     free(cur);
     return failed ? -1 : 0;
+}
+
+int orc_attn_naive(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                   int64_t n_edges, int32_t c, int32_t heads, int32_t layers,
+                   const double* w, const double* x, double* y)
+{
+    return orc_attn_layers(row_ptr, order, n_centres, n_edges, c, heads, layers, w, x, NULL, y);
+}
+
+/* Smooth attention: the same layers with the per-segment rescale by
+ * sum_j e_j / D~ (orc_layer_block); log_dt [layers][n_edges][heads]. */
+int orc_attn_smooth(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                    int64_t n_edges, int32_t c, int32_t heads, int32_t layers,
+                    const double* w, const double* x, const double* log_dt, double* y)
+{
+    if (!log_dt) return -1;
+    return orc_attn_layers(row_ptr, order, n_centres, n_edges, c, heads, layers, w, x, log_dt,
+                           y);
 }
 
 /*
@@ -373,7 +407,7 @@ int orc_attn_naive_centres(const int64_t* row_ptr, const int32_t* order,
                 memcpy(Xb + a * c, x + orc_edge_of(row_ptr, order, i, a) * c,
                        (size_t)c * sizeof(double));
             for (int32_t l = 0; l < layers; ++l) {
-                orc_layer_block(Xb, n, c, heads, w + (size_t)l * 4 * c * c, Yb, sc);
+                orc_layer_block(Xb, n, c, heads, w + (size_t)l * 4 * c * c, NULL, Yb, sc);
                 memcpy(Xb, Yb, (size_t)n * c * sizeof(double));
             }
             for (int64_t a = 0; a < n; ++a)

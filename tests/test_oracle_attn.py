@@ -161,3 +161,79 @@ def test_empty_rows_and_empty_input(oracle_mod):
     assert np.all(np.isfinite(y))
     y0 = oracle_mod.attn_naive(np.zeros(3, np.int64), np.zeros((0, 8)), w, 2)
     assert y0.shape == (0, 8)
+
+
+# --- smooth attention: w_j = softmax_j * (sum_j e_j / D~), a per-segment rescale -------------
+
+def _lse_per_segment(row_ptr, x, w, heads):
+    """ln sum_j exp(s_j) per (query edge, head) of a single layer, from torch's logsumexp over
+    scores formed by torch matmuls (a library routine, independent of the oracle's loops)."""
+    e, c = x.shape
+    d = c // heads
+    xt = torch.from_numpy(x)
+    q, k = xt @ torch.from_numpy(w[0, 0]), xt @ torch.from_numpy(w[0, 1])
+    out = np.zeros((1, e, heads))
+    for i in range(row_ptr.shape[0] - 1):
+        r0, r1 = int(row_ptr[i]), int(row_ptr[i + 1])
+        if r1 == r0:
+            continue
+        for h in range(heads):
+            sl = slice(h * d, (h + 1) * d)
+            s = (q[r0:r1, sl] @ k[r0:r1, sl].T) / math.sqrt(d)
+            out[0, r0:r1, h] = torch.logsumexp(s, dim=1).numpy()
+    return out
+
+
+def test_smooth_with_dtilde_equal_to_the_segment_sum_is_vanilla(oracle_mod):
+    """D~ = sum_j e_j makes the rescale 1: the smooth form reduces to plain softmax."""
+    row_ptr, x, w = _case(25, 30, 16, 1, 61, min_len=1)
+    ldt = _lse_per_segment(row_ptr, x, w, heads=4)
+    y = oracle_mod.attn_smooth(row_ptr, x, w, 4, ldt)
+    assert _normwise(y, oracle_mod.attn_naive(row_ptr, x, w, 4)) < 1e-13
+
+
+def test_smooth_rescale_is_per_segment_and_exponential(oracle_mod):
+    """Raising ln D~ by delta on one (query edge, head) segment scales only that segment's
+    head output, by exp(-delta): with Wo = I the output columns of head h are o_h itself."""
+    row_ptr, x, w = _case(12, 20, 12, 1, 62, min_len=2)
+    w[0, 3] = np.eye(12)
+    ldt = _lse_per_segment(row_ptr, x, w, heads=3) + 0.3
+    base = oracle_mod.attn_smooth(row_ptr, x, w, 3, ldt)
+    ldt2 = ldt.copy()
+    edge, head, delta = 7, 1, 1.7
+    ldt2[0, edge, head] += delta
+    y = oracle_mod.attn_smooth(row_ptr, x, w, 3, ldt2)
+    expect = base.copy()
+    expect[edge, 4 * head:4 * head + 4] *= math.exp(-delta)
+    assert _normwise(y, expect) < 1e-14
+    # and D~ above the segment sum by e^0.3 scales the vanilla output by e^-0.3
+    assert _normwise(base, math.exp(-0.3) * oracle_mod.attn_naive(row_ptr, x, w, 3)) < 1e-13
+
+
+def test_smooth_single_edge_closed_form(oracle_mod):
+    """n_i = 1: the one weight is e / D~ = exp(s - ln D~) with s = (x Wq).(x Wk)/sqrt(d) per
+    head, so y = [exp(s_h - ln D~_h) (x Wv)_h]_h Wo."""
+    x = W.make_features(4, 8, 5)
+    w = W.make_weights(1, 8, 6)
+    row_ptr = np.arange(5, dtype=np.int64)
+    ldt = np.random.default_rng(7).normal(0.0, 1.0, (1, 4, 2))
+    y = oracle_mod.attn_smooth(row_ptr, x, w, 2, ldt)
+    q, k, v = x @ w[0, 0], x @ w[0, 1], x @ w[0, 2]
+    o = np.zeros_like(v)
+    for a in range(4):
+        for h in range(2):
+            sl = slice(4 * h, 4 * h + 4)
+            s = float(q[a, sl] @ k[a, sl]) / 2.0
+            o[a, sl] = math.exp(s - ldt[0, a, h]) * v[a, sl]
+    assert _normwise(y, o @ w[0, 3]) < 1e-14
+
+
+def test_smooth_layers_take_their_own_dtilde(oracle_mod):
+    """Layer l reads ln D~[l]: a shift of layer 1's values leaves layer 0 alone, and with one
+    layer the smooth form of a two-layer stack's first layer is the one-layer result."""
+    row_ptr, x, w = _case(10, 15, 8, 2, 63, min_len=1)
+    ldt = np.random.default_rng(64).normal(2.0, 0.5, (2, x.shape[0], 2))
+    y2 = oracle_mod.attn_smooth(row_ptr, x, w, 2, ldt)
+    y1 = oracle_mod.attn_smooth(row_ptr, x, w[:1], 2, ldt[:1])
+    y12 = oracle_mod.attn_smooth(row_ptr, y1, w[1:], 2, ldt[1:])
+    assert _normwise(y2, y12) < 1e-14
