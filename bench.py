@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--pair-steps", type=int, default=2)
     ap.add_argument("--pair-chunk", type=int, default=1 << 26,
                     help="pairs per chunk of the pair-axis route")
+    ap.add_argument("--smooth", action="store_true",
+                    help="also time block_attn_forward_smooth (per-segment softmax rescale, "
+                         "ln D~ = ln n_i + 1.5) on the same inputs, after the timed steps")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter scaling)")
@@ -229,6 +232,29 @@ def main():
                       ev[2].elapsed_time(ev[3])] for ev in events])
     nl_ms, csr_ms, attn_ms = (float(v) for v in part.mean(axis=0))
 
+    smooth_rec = None
+    if args.smooth:
+        counts = np.diff(rp)
+        ldt_np = np.repeat(np.log(np.maximum(counts, 1)) + 1.5, counts)
+        ldt = torch.from_numpy(np.ascontiguousarray(np.broadcast_to(
+            ldt_np[None, :, None], (w.layers, e, w.heads)))).to(dev, x.dtype)
+        ys = torch.empty_like(x)
+        for _ in range(args.warmup):
+            nga.block_attn_forward(csr_out["row_ptr"], x, wt, w.heads, w.sel, y=ys, ws=ws_attn,
+                                   log_dtilde=ldt)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            nga.block_attn_forward(csr_out["row_ptr"], x, wt, w.heads, w.sel, y=ys, ws=ws_attn,
+                                   log_dtilde=ldt)
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        nga.check_status(ws_attn, "block_attn_forward_smooth")
+        sm_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        smooth_rec = {"ms_per_forward": sm_ms, "vs_block_attn_forward": sm_ms / attn_ms,
+                      "log_dtilde": "ln(n_i) + 1.5 for every edge and head of centre i"}
+
     pair_rec = None
     if args.pair_axis:
         pair_rec = time_pair_axis(nga, torch, dev, stream, csr_out["row_ptr"][: n + 1], x, wt, w,
@@ -282,6 +308,8 @@ def main():
         "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
                    "frac": nl_gbs / PEAK_HBM_GBS},
     }
+    if smooth_rec is not None:
+        rec["smooth"] = smooth_rec
     if pair_rec is not None:
         rec["pair_axis"] = pair_rec
     if not args.no_cpu_baseline:

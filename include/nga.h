@@ -7,6 +7,7 @@
  *   nl_build            O(N) cell-list neighbour rows under periodic boundaries
  *   edge_csr            those rows as a destination CSR with image shifts
  *   block_attn_forward  block-dense multi-head attention through the CSR
+ *   block_attn_forward_smooth  the same with a per-segment softmax rescale
  *   pair_attn_forward   the same attention by the ragged pair-axis route
  *                       (a measured comparator)
  *
@@ -60,7 +61,8 @@ enum {
     NGA_EDTYPE = -5,     /* unsupported dtype */
     NGA_EWORKSPACE = -6, /* workspace missing or smaller than the query returned */
     NGA_EHIP = -7,       /* HIP runtime error */
-    NGA_EINDEX = -8      /* an index in device data is out of range */
+    NGA_EINDEX = -8,     /* an index in device data is out of range */
+    NGA_ERANGE = -9      /* a smooth-attention rescale is beyond the kernel's range */
 };
 
 enum { NGA_F64 = 0, NGA_F32 = 1 };
@@ -188,6 +190,28 @@ int block_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
                        int64_t n_centres, int64_t n_edges, int32_t nnei_cap, int32_t c,
                        int32_t n_heads, int32_t n_layers, const void* weights, const void* x,
                        void* y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Smooth attention: block_attn_forward with each (query edge, head) segment's
+ * softmax rescaled by sum_j e_j / D~, the occupancy-modified weights
+ * w_j = softmax_j * (sum_j e_j / D~) of [P2] "Graph-native alternatives"
+ * (a per-segment scalar rescale of the vanilla softmax, D~ computed outside
+ * the attention).  With e_j = exp(s_j), this is w_j = exp(s_j - ln D~).
+ *
+ * log_dtilde  [n_layers][n_edges][n_heads] in the dtype of x: ln D~ of the
+ *             segment whose query is edge row e (the row of x and y) and
+ *             head h, at [l][e][h].  Must not be NULL when n_edges > 0.
+ * Other arguments as block_attn_forward.  ln D~ equal to the segment's
+ * log-sum-exp gives exactly the vanilla result.  The fp32 fused kernel
+ * holds the rescaled head outputs as f16 pairs with 2^9 of headroom: a
+ * factor sum_j e_j / D~ beyond about 2^9 sets NGA_ERANGE (device-detected;
+ * other paths have no such limit).
+ */
+int block_attn_forward_smooth(int dtype, const int64_t* row_ptr, const int32_t* order,
+                              int64_t n_centres, int64_t n_edges, int32_t nnei_cap, int32_t c,
+                              int32_t n_heads, int32_t n_layers, const void* weights,
+                              const void* x, const void* log_dtilde, void* y, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Ragged pair-axis attention (measured comparator)                          */

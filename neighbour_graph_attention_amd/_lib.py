@@ -17,13 +17,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnga.so")
 
 NGA_OK, NGA_EINVAL, NGA_EBOX, NGA_EROWCAP, NGA_ECAP, NGA_EDTYPE, NGA_EWORKSPACE, NGA_EHIP, \
-    NGA_EINDEX = 0, -1, -2, -3, -4, -5, -6, -7, -8
+    NGA_EINDEX, NGA_ERANGE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 NGA_F64, NGA_F32 = 0, 1
 ROW_CAP = 512
 
 EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "edge_csr",
            "block_attn_workspace_bytes", "block_attn_forward", "nga_sync_status", "nga_strerror",
-           "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward")
+           "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward",
+           "block_attn_forward_smooth")
 
 
 class NGAError(RuntimeError):
@@ -58,6 +59,9 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward.restype = ctypes.c_int
     lib.block_attn_forward.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32, vp, vp,
                                        vp, vp, sz, vp]
+    lib.block_attn_forward_smooth.restype = ctypes.c_int
+    lib.block_attn_forward_smooth.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32,
+                                              vp, vp, vp, vp, vp, sz, vp]
     lib.pair_attn_workspace_bytes.restype = sz
     lib.pair_attn_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32, i32, i32, i64]
     lib.pair_attn_forward.restype = ctypes.c_int
@@ -254,8 +258,11 @@ def attn_variant(dtype: int, nnei_cap: int, c: int, n_heads: int) -> str:
 
 def block_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Tensor,
                        n_heads: int, nnei_cap: int, *, order: torch.Tensor | None = None,
-                       y: torch.Tensor | None = None, ws: Workspace | None = None):
-    """Stacked block-dense attention layers; returns y [E][c] (same dtype as x)."""
+                       y: torch.Tensor | None = None, ws: Workspace | None = None,
+                       log_dtilde: torch.Tensor | None = None):
+    """Stacked block-dense attention layers; returns y [E][c] (same dtype as x).  With
+    log_dtilde ([layers][E][n_heads], ln D~ per query edge and head) the smooth form,
+    block_attn_forward_smooth, runs instead."""
     lib = load()
     dev = x.device
     e, c = x.shape
@@ -276,10 +283,18 @@ def block_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Te
         y = torch.empty_like(x)
     _need(y, "y", x.dtype, (e, c), dev)
     ws = _ws(ws, dev, block_attn_workspace_bytes(dt, e, nnei_cap, c, n_heads, layers))
-    rc = lib.block_attn_forward(dt, _ptr(row_ptr), _ptr(order), n_centres, e, int(nnei_cap), c,
-                                int(n_heads), int(layers), _ptr(weights), _ptr(x), _ptr(y),
-                                ws.ptr(), ws.nbytes, _stream(dev))
-    _check(rc, "block_attn_forward")
+    if log_dtilde is None:
+        rc = lib.block_attn_forward(dt, _ptr(row_ptr), _ptr(order), n_centres, e, int(nnei_cap),
+                                    c, int(n_heads), int(layers), _ptr(weights), _ptr(x), _ptr(y),
+                                    ws.ptr(), ws.nbytes, _stream(dev))
+        _check(rc, "block_attn_forward")
+    else:
+        _need(log_dtilde, "log_dtilde", x.dtype, (layers, e, int(n_heads)), dev)
+        rc = lib.block_attn_forward_smooth(dt, _ptr(row_ptr), _ptr(order), n_centres, e,
+                                           int(nnei_cap), c, int(n_heads), int(layers),
+                                           _ptr(weights), _ptr(x), _ptr(log_dtilde), _ptr(y),
+                                           ws.ptr(), ws.nbytes, _stream(dev))
+        _check(rc, "block_attn_forward_smooth")
     return y
 
 

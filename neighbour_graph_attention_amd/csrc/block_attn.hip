@@ -44,6 +44,8 @@ struct CoreArgs {
     int heads;
     int d;
     T scale;
+    const T* ldt;          // smooth attention: this layer's ln D~ [n_edges][heads], or NULL
+    const int32_t* order;  // edge row of each slot (NULL: the slot itself), for ldt
     uint32_t* status;
 };
 
@@ -94,9 +96,16 @@ __global__ void __launch_bounds__(256) attn_core_kernel(CoreArgs<T> A) {
                 if (t < d) acc[t] += p * vb[t];
         }
         T* out = A.o + (r0 + a) * c + h * d;
+        // Smooth attention: sum_j e_j / D~ times the softmax = exp(s_j - ln D~), i.e. the
+        // weighted sum times exp(m - ln D~) in place of 1/Z.
+        T f = T(0);
+        if (A.ldt) {
+            const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+            if (row >= 0 && row < A.n_edges) f = exp_t<T>(m - A.ldt[row * A.heads + h]);
+        }
 #pragma unroll
         for (int t = 0; t < DMAX; ++t)
-            if (t < d) out[t] = acc[t] / z;
+            if (t < d) out[t] = A.ldt ? acc[t] * f : acc[t] / z;
     }
 }
 
@@ -136,7 +145,7 @@ int launch_core(const CoreArgs<T>& A, hipStream_t s) {
 template <typename T>
 int run_generic(const int64_t* row_ptr, const int32_t* order, int64_t n_centres, int64_t n_edges,
                 int32_t nnei_cap, int32_t c, int32_t heads, int32_t layers, const T* weights,
-                const T* x, T* y, void* ws, hipStream_t s) {
+                const T* x, const T* ldt, T* y, void* ws, hipStream_t s) {
     GenericWs w = carve_generic(ws, n_edges, c, layers, sizeof(T));
     uint32_t* status = &static_cast<WsHeader*>(ws)->status;
     const int64_t* e_dev = row_ptr + n_centres;
@@ -173,6 +182,8 @@ int run_generic(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
         A.heads = heads;
         A.d = d;
         A.scale = T(1) / std::sqrt(T(d));
+        A.ldt = ldt ? ldt + (size_t)l * n_edges * heads : nullptr;
+        A.order = order;
         A.status = status;
         if ((rc = launch_core(A, s))) return rc;
         GemmArgs<T> g2 = g1;
@@ -218,12 +229,13 @@ extern "C" const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, 
     return dtype == NGA_F64 ? "generic_f64" : "generic_f32";
 }
 
-extern "C" int block_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
-                                  int64_t n_centres, int64_t n_edges, int32_t nnei_cap,
-                                  int32_t c, int32_t n_heads, int32_t n_layers,
-                                  const void* weights, const void* x, void* y, void* ws,
-                                  size_t ws_bytes, void* stream) {
-    using namespace nga;
+namespace nga {
+namespace {
+
+int attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                 int64_t n_edges, int32_t nnei_cap, int32_t c, int32_t n_heads, int32_t n_layers,
+                 const void* weights, const void* x, const void* ldt, void* y, void* ws,
+                 size_t ws_bytes, void* stream) {
     if (dtype != NGA_F64 && dtype != NGA_F32) return NGA_EDTYPE;
     if (n_centres < 0 || n_centres >= INT32_MAX || n_edges < 0 || nnei_cap < 1 || c < 1 ||
         n_heads < 1 || c % n_heads != 0 || n_layers < 1)
@@ -247,7 +259,7 @@ extern "C" int block_attn_forward(int dtype, const int64_t* row_ptr, const int32
         Carver cv(ws);
         float* packed = cv.take<float>(fused_workspace_floats(c, n_layers));
         return run_fused(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
-                         weights, x, y, packed, status, s);
+                         weights, x, ldt, y, packed, status, s);
     }
     hipLaunchKernelGGL(check_rows_kernel, dim3(1), dim3(1), 0, s, row_ptr, (int)n_centres, n_edges,
                        status);
@@ -257,14 +269,39 @@ extern "C" int block_attn_forward(int dtype, const int64_t* row_ptr, const int32
         GenericWs w = carve_generic(ws, n_edges, c, n_layers, sizeof(double));
         return run_f64_mfma(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
                             static_cast<const double*>(weights), static_cast<const double*>(x),
-                            static_cast<double*>(y), static_cast<double*>(w.qkv),
+                            static_cast<const double*>(ldt), static_cast<double*>(y),
+                            static_cast<double*>(w.qkv),
                             static_cast<double*>(w.o), static_cast<double*>(w.xbuf), status, s);
     }
     if (dtype == NGA_F64)
         return run_generic<double>(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads,
                                    n_layers, static_cast<const double*>(weights),
-                                   static_cast<const double*>(x), static_cast<double*>(y), ws, s);
+                                   static_cast<const double*>(x), static_cast<const double*>(ldt),
+                                   static_cast<double*>(y), ws, s);
     return run_generic<float>(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
                               static_cast<const float*>(weights), static_cast<const float*>(x),
-                              static_cast<float*>(y), ws, s);
+                              static_cast<const float*>(ldt), static_cast<float*>(y), ws, s);
+}
+
+}  // namespace
+}  // namespace nga
+
+extern "C" int block_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
+                                  int64_t n_centres, int64_t n_edges, int32_t nnei_cap,
+                                  int32_t c, int32_t n_heads, int32_t n_layers,
+                                  const void* weights, const void* x, void* y, void* ws,
+                                  size_t ws_bytes, void* stream) {
+    return nga::attn_forward(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads,
+                             n_layers, weights, x, nullptr, y, ws, ws_bytes, stream);
+}
+
+extern "C" int block_attn_forward_smooth(int dtype, const int64_t* row_ptr, const int32_t* order,
+                                         int64_t n_centres, int64_t n_edges, int32_t nnei_cap,
+                                         int32_t c, int32_t n_heads, int32_t n_layers,
+                                         const void* weights, const void* x,
+                                         const void* log_dtilde, void* y, void* ws,
+                                         size_t ws_bytes, void* stream) {
+    if (n_edges > 0 && !log_dtilde) return NGA_EINVAL;
+    return nga::attn_forward(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads,
+                             n_layers, weights, x, log_dtilde, y, ws, ws_bytes, stream);
 }

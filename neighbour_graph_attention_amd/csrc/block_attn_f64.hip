@@ -136,6 +136,8 @@ struct CoreF64Args {
     int nnei_cap;
     int c;
     double scale;  // 1 / sqrt(d)
+    const double* ldt;     // smooth attention: this layer's ln D~ [n_edges][heads], or NULL
+    const int32_t* order;  // edge row of each slot (NULL: the slot itself), for ldt
     uint32_t* status;
 };
 
@@ -226,6 +228,14 @@ __global__ void __launch_bounds__(256) attn_core_f64_kernel(CoreF64Args A) {
         }
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
+        // Smooth attention: sum_j e_j / D~ times the softmax = exp(s_j - ln D~), i.e. the
+        // weighted sum times exp(m - ln D~) in place of 1/Z.
+        double f = 0.0;
+        if (A.ldt && a < n) {
+            const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+            if (row >= 0 && row < A.n_edges)
+                f = exp(m * A.scale - A.ldt[row * gridDim.y + h]);
+        }
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
             d4 acc = {0.0, 0.0, 0.0, 0.0};
@@ -244,7 +254,8 @@ __global__ void __launch_bounds__(256) attn_core_f64_kernel(CoreF64Args A) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * dt + gq + 4 * r;
-                if (a < n && t < D) A.o[(r0 + a) * c + h * D + t] = acc[r] / z;
+                if (a < n && t < D)
+                    A.o[(r0 + a) * c + h * D + t] = A.ldt ? acc[r] * f : acc[r] / z;
             }
         }
     }
@@ -276,8 +287,8 @@ bool f64_mfma_supported(int32_t nnei_cap, int32_t c, int32_t heads) {
 
 int run_f64_mfma(const int64_t* row_ptr, const int32_t* order, int64_t n_centres, int64_t n_edges,
                  int32_t nnei_cap, int32_t c, int32_t heads, int32_t layers, const double* weights,
-                 const double* x, double* y, double* qkv, double* o, double* xbuf,
-                 uint32_t* status, hipStream_t s) {
+                 const double* x, const double* log_dtilde, double* y, double* qkv, double* o,
+                 double* xbuf, uint32_t* status, hipStream_t s) {
     const int64_t* e_dev = row_ptr + n_centres;
     const size_t cc = (size_t)c * c;
     const int d = c / heads;
@@ -306,6 +317,8 @@ int run_f64_mfma(const int64_t* row_ptr, const int32_t* order, int64_t n_centres
         a.nnei_cap = nnei_cap;
         a.c = c;
         a.scale = 1.0 / std::sqrt((double)d);
+        a.ldt = log_dtilde ? log_dtilde + (size_t)l * n_edges * heads : nullptr;
+        a.order = order;
         a.status = status;
         if ((rc = launch_core(a, n_centres, heads, d, s))) return rc;
         GemmF64Args g2 = g1;

@@ -134,8 +134,15 @@ struct FusedArgs {
     int64_t n_edges;
     int nnei_cap;
     int layers;
+    const float* ldt;  // smooth attention: ln D~ [layers][n_edges][H], or NULL
     uint32_t* status;
 };
+
+// Smooth attention rescales each (query, head) output by sum_j e_j / D~, so O is no longer a
+// convex combination of V rows.  Its instances lower the output scale by 2^8, which leaves
+// room for factors up to about 2^9 in the split, and report anything past kSplitMax.
+constexpr int kSmoothHeadroom = 8;
+constexpr float kSplitMax = 32768.f;
 
 // LDS block row: 64 hi halves, 64 lo halves, 16 bytes of padding (272 bytes) -- or, between
 // layers, the row's C floats.
@@ -180,7 +187,7 @@ __device__ inline h8 dup_read(const unsigned char* p) {
     return h8{v[0], v[1], v[2], v[3], v[0], v[1], v[2], v[3]};
 }
 
-template <int H, int NT>
+template <int H, int NT, bool SMOOTH>
 __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __restrict__ P,
                                              const int layer, const int ex, const int64_t r0,
                                              const int n, const bool last,
@@ -252,7 +259,7 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
     vmax = red[0];
 #pragma unroll
     for (int w = 1; w < H; ++w) vmax = fmaxf(vmax, red[w]);
-    const int e_o = scale_exponent(vmax);
+    const int e_o = scale_exponent(vmax) - (SMOOTH ? kSmoothHeadroom : 0);
     const float yscale = ldexpf(1.f, -(ex + ev + e_o + eo));
     // V at that scale, split: lane (i, g) of key tile t holds [V_hi, V_lo] of keys
     // 16t + 4g .. 16t + 4g + 3, channel i -- the A operand of O^T = V^T P^T.
@@ -319,7 +326,23 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
             osum = mfma16(va[t], pa, osum);
             osum = mfma16(va[t], swap_halves(pa), osum);
         }
-        const f4 o = osum * __builtin_amdgcn_rcpf(z);
+        f4 o;
+        if constexpr (SMOOTH) {
+            // sum_j e_j / D~ times the softmax = exp(s_j - ln D~): in place of 1/Z,
+            // exp2(m c1 - 13 - log2(e) ln D~) (P carries 2^13 and the row max).
+            const int aq = 16 * qt + li;
+            float f = 0.f;
+            if (aq < n) {
+                const int64_t row = A.order ? (int64_t)A.order[r0 + aq] : r0 + aq;
+                if (row >= 0 && row < A.n_edges)
+                    f = exp2f(mc - kLog2e * A.ldt[((int64_t)layer * A.n_edges + row) * H + h]);
+            }
+            o = osum * f;
+            const float om = fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3])));
+            if (!(om <= kSplitMax)) raise_bits(A.status, kBitRange);
+        } else {
+            o = osum * __builtin_amdgcn_rcpf(z);
+        }
 
         h8 os;
 #pragma unroll
@@ -394,7 +417,7 @@ __device__ inline int split_block(f4 (&vals)[PER], int chunks, unsigned char* sX
     return e;
 }
 
-template <int H, int TMAX>
+template <int H, int TMAX, bool SMOOTH>
 __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
     constexpr int C = 16 * H;
     constexpr int U = C / 16;
@@ -449,7 +472,8 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
 #define NGA_CASE(T)                                                                            \
     case T:                                                                                    \
         if constexpr (T <= TMAX)                                                               \
-            centre_layer<H, T>(A, P, layer, ex, r0, n, last, sX, sO, sWo[h], red, lane, h);        \
+            centre_layer<H, T, SMOOTH>(A, P, layer, ex, r0, n, last, sX, sO, sWo[h], red, lane,  \
+                                       h);                                                     \
         break;
             switch (nt) {
                 NGA_CASE(1) NGA_CASE(2) NGA_CASE(3) NGA_CASE(4) NGA_CASE(5) NGA_CASE(6)
@@ -477,13 +501,21 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
     if (bad_index) raise_bits(A.status, kBitIndex);
 }
 
+template <int H, bool SMOOTH>
+int launch_hs(int tmax, const FusedArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_centres), block(64 * H);
+    if (tmax <= 4)
+        hipLaunchKernelGGL((fused_f32_d16_kernel<H, 4, SMOOTH>), grid, block, 0, s, a);
+    else if (tmax <= 8)
+        hipLaunchKernelGGL((fused_f32_d16_kernel<H, 8, SMOOTH>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((fused_f32_d16_kernel<H, 12, SMOOTH>), grid, block, 0, s, a);
+    return last_launch_status();
+}
+
 template <int H>
 int launch_h(int tmax, const FusedArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)a.n_centres), block(64 * H);
-    if (tmax <= 4) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 4>), grid, block, 0, s, a);
-    else if (tmax <= 8) hipLaunchKernelGGL((fused_f32_d16_kernel<H, 8>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fused_f32_d16_kernel<H, 12>), grid, block, 0, s, a);
-    return last_launch_status();
+    return a.ldt ? launch_hs<H, true>(tmax, a, s) : launch_hs<H, false>(tmax, a, s);
 }
 
 }  // namespace
@@ -504,8 +536,8 @@ size_t fused_workspace_floats(int32_t c, int32_t layers) { return (size_t)layers
 
 int run_fused(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
               int64_t n_edges, int32_t nnei_cap, int32_t c, int32_t heads, int32_t layers,
-              const void* weights, const void* x, void* y, void* packed, uint32_t* status,
-              hipStream_t s) {
+              const void* weights, const void* x, const void* log_dtilde, void* y, void* packed,
+              uint32_t* status, hipStream_t s) {
     (void)dtype;
     float* pk = static_cast<float*>(packed);
     int* expo = reinterpret_cast<int*>(pk + (size_t)layers * 4 * c * c);
@@ -524,6 +556,7 @@ int run_fused(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n
     a.n_edges = n_edges;
     a.nnei_cap = nnei_cap;
     a.layers = layers;
+    a.ldt = static_cast<const float*>(log_dtilde);
     a.status = status;
     const int tmax = (nnei_cap + 15) / 16;
     switch (heads) {
