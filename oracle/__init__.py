@@ -61,6 +61,8 @@ def _load():
         fn.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp]
     lib.orc_attn_smooth.restype = ctypes.c_int
     lib.orc_attn_smooth.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.orc_local_atten.restype = ctypes.c_int
+    lib.orc_local_atten.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.orc_attn_naive_centres.restype = ctypes.c_int
     lib.orc_attn_naive_centres.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp]
     lib.orc_num_threads.restype = ctypes.c_int
@@ -174,6 +176,24 @@ def attn_smooth(row_ptr, x, w, heads: int, log_dtilde, order=None):
     if rc != 0:
         raise ValueError("oracle attn_smooth failed")
     return y
+
+
+def local_atten(row_ptr, xc, x, w, heads: int, order=None):
+    """LocalAtten: one query per centre (xc [N][c]) over the centre's edges (x [E][c]) as keys
+    and values; stacked layers update xc.  Returns yc [N][c]."""
+    lib = _load()
+    row_ptr, order, x, w = _attn_args(row_ptr, order, x, w)
+    xc = _f64(xc)
+    e, c = x.shape
+    n = row_ptr.shape[0] - 1
+    if xc.shape != (n, c):
+        raise ValueError("xc must be [n_centres][c]")
+    yc = np.zeros_like(xc)
+    rc = lib.orc_local_atten(_ptr(row_ptr), _ptr(order), n, e, c, heads, w.shape[0], _ptr(w),
+                             _ptr(xc), _ptr(x), _ptr(yc))
+    if rc != 0:
+        raise ValueError("oracle local_atten failed")
+    return yc
 
 
 def attn_naive_centres(row_ptr, x, w, heads: int, centres, order=None):

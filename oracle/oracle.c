@@ -518,6 +518,92 @@ done:
     return rc;
 }
 
+/*
+ * LocalAtten: attention with the centres as queries and each centre's edges
+ * as keys and values, one query per segment ([P2] "Graph-native
+ * alternatives": LocalAtten maps directly to varlen attention with queries =
+ * centers, keys = edges; [P2] "Measurements" names it among the DPA-2 graph
+ * attention ops).  For each layer l with weights (Wq, Wk, Wv, Wo) and each
+ * centre i with edges e_0 .. e_{n-1} (order-mapped as in orc_attn_naive):
+ *   q = xc_i Wq,  k_a = x_{e_a} Wk,  v_a = x_{e_a} Wv
+ *   head h (columns h*d .. h*d+d-1):
+ *     s_a = (q . k_a)_h / sqrt(d),  m = max_a s_a,  p_a = exp(s_a - m),
+ *     o[h cols] = (sum_a p_a v_a[h cols]) / sum_a p_a
+ *   yc_i = o Wo
+ * Stacked layers update the centre features only, xc <- yc; the edge
+ * features x are the keys and values of every layer.  A centre with no edges
+ * has no softmax; its output is o = 0, so yc_i = 0.
+ * xc, yc: [n_centres][c]; x: [n_edges][c]; w: [layers][4][c][c].
+ * Returns 0, or -1 on bad arguments / out of memory.
+ */
+int orc_local_atten(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                    int64_t n_edges, int32_t c, int32_t heads, int32_t layers,
+                    const double* w, const double* xc, const double* x, double* yc)
+{
+    if (c < 1 || heads < 1 || c % heads != 0 || layers < 1 || n_centres < 0 || n_edges < 0)
+        return -1;
+    const int64_t cc = (int64_t)c * c;
+    const int32_t d = c / heads;
+    const double scale = 1.0 / sqrt((double)d);
+    const int64_t nmax = orc_max_row(row_ptr, n_centres);
+    double* cur = (double*)malloc((size_t)(n_centres > 0 ? n_centres : 1) * c * sizeof(double));
+    if (!cur) return -1;
+    memcpy(cur, xc, (size_t)n_centres * c * sizeof(double));
+    int failed = 0;
+    for (int32_t l = 0; l < layers && !failed; ++l) {
+        const double* W = w + (size_t)l * 4 * cc;
+#pragma omp parallel reduction(| : failed)
+        {
+            double* Xb = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
+            double* k = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
+            double* v = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
+            double* s = (double*)malloc((size_t)(nmax + 1) * sizeof(double));
+            double* q = (double*)malloc((size_t)c * sizeof(double));
+            double* o = (double*)malloc((size_t)c * sizeof(double));
+            if (!Xb || !k || !v || !s || !q || !o) failed = 1;
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t i = 0; i < n_centres; ++i) {
+                if (failed) continue;
+                const int64_t n = row_ptr[i + 1] - row_ptr[i];
+                for (int32_t t = 0; t < c; ++t) o[t] = 0.0;
+                if (n > 0) {
+                    for (int64_t a = 0; a < n; ++a)
+                        memcpy(Xb + a * c, x + orc_edge_of(row_ptr, order, i, a) * c,
+                               (size_t)c * sizeof(double));
+                    orc_matmul(cur + i * c, 1, c, W + 0 * cc, q);
+                    orc_matmul(Xb, n, c, W + 1 * cc, k);
+                    orc_matmul(Xb, n, c, W + 2 * cc, v);
+                    for (int32_t h = 0; h < heads; ++h) {
+                        const int32_t c0 = h * d;
+                        double m = -INFINITY;
+                        for (int64_t a = 0; a < n; ++a) {
+                            double dot = 0.0;
+                            for (int32_t t = 0; t < d; ++t) dot += q[c0 + t] * k[a * c + c0 + t];
+                            s[a] = dot * scale;
+                            if (s[a] > m) m = s[a];
+                        }
+                        double z = 0.0;
+                        for (int64_t a = 0; a < n; ++a) {
+                            s[a] = exp(s[a] - m);
+                            z += s[a];
+                        }
+                        for (int32_t t = 0; t < d; ++t) {
+                            double acc = 0.0;
+                            for (int64_t a = 0; a < n; ++a) acc += s[a] * v[a * c + c0 + t];
+                            o[c0 + t] = acc / z;
+                        }
+                    }
+                }
+                orc_matmul(o, 1, c, W + 3 * cc, yc + i * c);
+            }
+            free(Xb); free(k); free(v); free(s); free(q); free(o);
+        }
+        if (l + 1 < layers) memcpy(cur, yc, (size_t)n_centres * c * sizeof(double));
+    }
+    free(cur);
+    return failed ? -1 : 0;
+}
+
 /* Threads the OpenMP loops above use (1 without OpenMP). */
 int orc_num_threads(void)
 {
