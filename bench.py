@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--smooth", action="store_true",
                     help="also time block_attn_forward_smooth (per-segment softmax rescale, "
                          "ln D~ = ln n_i + 1.5) on the same inputs, after the timed steps")
+    ap.add_argument("--local-atten", action="store_true",
+                    help="also time local_attn_forward (LocalAtten: one query per centre over "
+                         "its edges, random centre rows) on the same CSR and edge features")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter scaling)")
@@ -255,6 +258,29 @@ def main():
         smooth_rec = {"ms_per_forward": sm_ms, "vs_block_attn_forward": sm_ms / attn_ms,
                       "log_dtilde": "ln(n_i) + 1.5 for every edge and head of centre i"}
 
+    local_rec = None
+    if args.local_atten:
+        xc = torch.from_numpy(W.make_features(n, w.c, 600, x_np.dtype)).to(dev)
+        yc = torch.empty_like(xc)
+        ws_loc = nga.Workspace(dev)
+        for _ in range(args.warmup):
+            nga.local_attn_forward(csr_out["row_ptr"], xc, x, wt, w.heads, yc=yc, ws=ws_loc)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            nga.local_attn_forward(csr_out["row_ptr"], xc, x, wt, w.heads, yc=yc, ws=ws_loc)
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        nga.check_status(ws_loc, "local_attn_forward")
+        loc_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        es = x.element_size()
+        # every layer reads the edge rows once; the centre rows are read and written once
+        loc_bytes = float(w.layers * e * w.c * es + 2 * n * w.c * es + 8 * (n + 1))
+        local_rec = {"ms_per_forward": loc_ms, "algorithmic_bytes": loc_bytes,
+                     "achieved_gbs": loc_bytes / (loc_ms * 1e-3) / 1e9,
+                     "frac_hbm": loc_bytes / (loc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
     pair_rec = None
     if args.pair_axis:
         pair_rec = time_pair_axis(nga, torch, dev, stream, csr_out["row_ptr"][: n + 1], x, wt, w,
@@ -310,6 +336,8 @@ def main():
     }
     if smooth_rec is not None:
         rec["smooth"] = smooth_rec
+    if local_rec is not None:
+        rec["local_atten"] = local_rec
     if pair_rec is not None:
         rec["pair_axis"] = pair_rec
     if not args.no_cpu_baseline:

@@ -8,6 +8,7 @@
  *   edge_csr            those rows as a destination CSR with image shifts
  *   block_attn_forward  block-dense multi-head attention through the CSR
  *   block_attn_forward_smooth  the same with a per-segment softmax rescale
+ *   local_attn_forward  LocalAtten: one query per centre over its edges
  *   pair_attn_forward   the same attention by the ragged pair-axis route
  *                       (a measured comparator)
  *
@@ -212,6 +213,39 @@ int block_attn_forward_smooth(int dtype, const int64_t* row_ptr, const int32_t* 
                               int32_t n_heads, int32_t n_layers, const void* weights,
                               const void* x, const void* log_dtilde, void* y, void* ws,
                               size_t ws_bytes, void* stream);
+
+/*
+ * LocalAtten: attention with the centres as queries and each centre's edges
+ * as keys and values, one query per segment ([P2] "Graph-native
+ * alternatives": queries = centers, keys = edges, destination_row_ptr as
+ * the segment offsets, streamed with the online-softmax recurrence).
+ *
+ * For each layer l with weights (Wq, Wk, Wv, Wo) and each centre i with
+ * edges e_0 .. e_{n-1} (e_a = order ? order[row_ptr[i] + a] : row_ptr[i] + a):
+ *   q = xc_i Wq,  k_a = x[e_a] Wk,  v_a = x[e_a] Wv
+ *   head h (columns h*d .. h*d+d-1, d = c / n_heads):
+ *     w = softmax over a of (q_h . k_a,h / sqrt(d)),  o_h = sum_a w_a v_a,h
+ *   yc_i = [o_0 .. o_{H-1}] Wo
+ * Stacked layers update the centre rows only (xc <- yc); x is the keys and
+ * values of every layer.  A centre without edges gets yc_i = 0.
+ *
+ * xc, yc      [n_centres][c]; must not alias.
+ * x           [n_edges][c] edge features; row_ptr / order as for
+ *             block_attn_forward (rows of any length).
+ * weights     [n_layers][4][c][c] (q, k, v, o), y = x W.
+ * c a multiple of 4 up to 256 and n_heads <= 16 (NGA_EINVAL otherwise).  The
+ * workspace holds two [n_centres][n_heads * c] buffers, two [n_heads * c][c]
+ * matrices per layer and, for several layers, one [n_centres][c] buffer.
+ * Device-detected: NGA_ECAP (row_ptr out of [0, n_edges] or decreasing),
+ * NGA_EINDEX (order out of range).
+ */
+size_t local_attn_workspace_bytes(int dtype, int64_t n_centres, int32_t c, int32_t n_heads,
+                                  int32_t n_layers);
+
+int local_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
+                       int64_t n_centres, int64_t n_edges, int32_t c, int32_t n_heads,
+                       int32_t n_layers, const void* weights, const void* xc, const void* x,
+                       void* yc, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Ragged pair-axis attention (measured comparator)                          */

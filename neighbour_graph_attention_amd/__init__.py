@@ -5,6 +5,7 @@ Python face of libnga.so, the C-ABI library declared in include/nga.h:
 * ``nl_build``: O(N) cell-list neighbour rows under periodic boundaries;
 * ``edge_csr``: those rows as a destination CSR with image shifts;
 * ``block_attn_forward``: block-dense multi-head attention through the CSR;
+* ``local_attn_forward``: LocalAtten, one query per centre over its edges;
 * ``pair_attn_forward``: the same attention by the ragged pair-axis route, a
   measured comparator.
 
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     edge_csr,
     load,
     nl_build,
+    local_attn_forward,
     nl_build_workspace_bytes,
     pair_attn_forward,
     pair_attn_workspace_bytes,

@@ -24,7 +24,7 @@ ROW_CAP = 512
 EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "edge_csr",
            "block_attn_workspace_bytes", "block_attn_forward", "nga_sync_status", "nga_strerror",
            "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward",
-           "block_attn_forward_smooth")
+           "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward")
 
 
 class NGAError(RuntimeError):
@@ -62,6 +62,11 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward_smooth.restype = ctypes.c_int
     lib.block_attn_forward_smooth.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32,
                                               vp, vp, vp, vp, vp, sz, vp]
+    lib.local_attn_workspace_bytes.restype = sz
+    lib.local_attn_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32]
+    lib.local_attn_forward.restype = ctypes.c_int
+    lib.local_attn_forward.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, vp, vp, vp,
+                                       vp, vp, sz, vp]
     lib.pair_attn_workspace_bytes.restype = sz
     lib.pair_attn_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i32, i32, i32, i64]
     lib.pair_attn_forward.restype = ctypes.c_int
@@ -338,3 +343,37 @@ def pair_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Ten
                                ws.ptr(), ws.nbytes, _stream(dev))
     _check(rc, "pair_attn_forward")
     return y
+
+
+def local_attn_forward(row_ptr: torch.Tensor, xc: torch.Tensor, x: torch.Tensor,
+                       weights: torch.Tensor, n_heads: int, *, order: torch.Tensor | None = None,
+                       yc: torch.Tensor | None = None, ws: Workspace | None = None):
+    """LocalAtten: one query per centre (xc [N][c]) over its edges (x [E][c]); returns
+    yc [N][c]."""
+    lib = load()
+    dev = x.device
+    e, c = x.shape
+    dt = _attn_dtype(x)
+    n_centres = row_ptr.shape[0] - 1
+    _need(row_ptr, "row_ptr", torch.int64, (n_centres + 1,), dev)
+    _need(xc, "xc", x.dtype, (n_centres, c), dev)
+    if weights.dim() != 4:
+        raise ValueError("weights must be [layers][4][c][c]")
+    layers = weights.shape[0]
+    _need(weights, "weights", x.dtype, (layers, 4, c, c), dev)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if order is not None:
+        if order.dim() != 1 or order.dtype != torch.int32 or order.device != dev or \
+                not order.is_contiguous():
+            raise ValueError("order must be a contiguous int32 vector on the device")
+    if yc is None:
+        yc = torch.empty_like(xc)
+    _need(yc, "yc", x.dtype, (n_centres, c), dev)
+    ws = _ws(ws, dev, int(lib.local_attn_workspace_bytes(dt, n_centres, c, int(n_heads),
+                                                         int(layers))))
+    rc = lib.local_attn_forward(dt, _ptr(row_ptr), _ptr(order), n_centres, e, c, int(n_heads),
+                                int(layers), _ptr(weights), _ptr(xc), _ptr(x), _ptr(yc),
+                                ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "local_attn_forward")
+    return yc

@@ -1,6 +1,7 @@
 // Row-gather / row-scatter GEMM on the vector ALUs, for any channel count and either
-// precision: out[out_rows(m)][u] = sum_t a[a_rows(m)][t] * W_{u / c}[t][u % c].  Used by the
-// generic attention path and by the pair-axis route.
+// precision: out[out_rows(m)][u] = sum_{t < k} a[a_rows(m)][t] * W_{u / c}[t][u % c], with nmat
+// matrices W of [k][c] side by side in the output columns (k = c unless set).  Used by the
+// generic attention path, the pair-axis route and LocalAtten.
 #pragma once
 
 #include "nga_internal.h"
@@ -17,10 +18,11 @@ struct GemmArgs {
     const T* w;             // nmat matrices [c][c] side by side in the output columns
     T* out;
     const int32_t* out_rows;  // nullable: row m of the result goes to out[out_rows[m]]
-    const int64_t* e_dev;     // rows m < *e_dev are computed
-    int64_t n_edges;          // bound on gathered / scattered row indices
-    int c;
+    const int64_t* e_dev;     // rows m < *e_dev are computed (NULL: all n_edges rows)
+    int64_t n_edges;          // bound on the rows and on gathered / scattered row indices
+    int c;                    // output columns per matrix
     int nmat;
+    int k = 0;                // reduction length (0: c)
     int lda;
     int ldo;
     uint32_t* status;
@@ -31,7 +33,8 @@ template <typename T>
 __global__ void __launch_bounds__(256) gemm_rows_kernel(GemmArgs<T> g) {
     __shared__ T sa[kGemmBK][kGemmBM + 1];
     __shared__ T sw[kGemmBK][kGemmBN + 1];
-    const int64_t E = *g.e_dev < g.n_edges ? *g.e_dev : g.n_edges;
+    const int64_t E = g.e_dev ? (*g.e_dev < g.n_edges ? *g.e_dev : g.n_edges) : g.n_edges;
+    const int K = g.k > 0 ? g.k : g.c;
     const int64_t m0 = (int64_t)blockIdx.x * kGemmBM;
     const int u0 = blockIdx.y * kGemmBN;
     if (m0 >= E) return;
@@ -42,12 +45,12 @@ __global__ void __launch_bounds__(256) gemm_rows_kernel(GemmArgs<T> g) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = T(0);
-    for (int k0 = 0; k0 < g.c; k0 += kGemmBK) {
+    for (int k0 = 0; k0 < K; k0 += kGemmBK) {
         for (int idx = threadIdx.x; idx < kGemmBM * kGemmBK; idx += 256) {
             int r = idx / kGemmBK, kk = idx % kGemmBK;
             int64_t m = m0 + r;
             T v = T(0);
-            if (m < E && k0 + kk < g.c) {
+            if (m < E && k0 + kk < K) {
                 int64_t row = g.a_rows ? (int64_t)g.a_rows[m] : m;
                 if (row >= 0 && row < g.n_edges) v = g.a[row * g.lda + k0 + kk];
             }
@@ -57,9 +60,9 @@ __global__ void __launch_bounds__(256) gemm_rows_kernel(GemmArgs<T> g) {
             int kk = idx / kGemmBN, cc = idx % kGemmBN;
             int u = u0 + cc, t = k0 + kk;
             T v = T(0);
-            if (u < nout && t < g.c) {
+            if (u < nout && t < K) {
                 int mat = u / g.c, col = u % g.c;
-                v = g.w[(int64_t)mat * g.c * g.c + (int64_t)t * g.c + col];
+                v = g.w[((int64_t)mat * K + t) * g.c + col];
             }
             sw[kk][cc] = v;
         }

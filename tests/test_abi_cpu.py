@@ -153,6 +153,34 @@ def test_pair_attn_rejects_bad_arguments():
     assert lib.pair_attn_workspace_bytes(L.NGA_F32, 100, 1000, 64, 4, 1, 0) == 0
 
 
+def test_local_attn_rejects_bad_arguments():
+    lib = nga.load()
+
+    def call(dt=L.NGA_F32, nc=4, ne=40, c=16, h=4, layers=1, rp=FAKE, w=FAKE,
+             xc=0x100000, x=0x500000, yc=0x900000, ws=FAKE, wsb=1 << 40):
+        return lib.local_attn_forward(dt, rp, None, nc, ne, c, h, layers, w,
+                                      ctypes.c_void_p(xc), ctypes.c_void_p(x),
+                                      ctypes.c_void_p(yc), ws, wsb, None)
+
+    assert call(dt=7) == L.NGA_EDTYPE
+    assert call(c=18, h=4) == L.NGA_EINVAL           # c not divisible by heads
+    assert call(c=512, h=4) == L.NGA_EINVAL          # c above 256
+    assert call(c=6, h=2) == L.NGA_EINVAL            # c not a multiple of 4
+    assert call(c=64, h=32) == L.NGA_EINVAL          # more than 16 heads
+    assert call(h=0) == L.NGA_EINVAL
+    assert call(layers=0) == L.NGA_EINVAL
+    assert call(rp=None) == L.NGA_EINVAL
+    assert call(w=None) == L.NGA_EINVAL
+    assert call(yc=0x100000 + 8) == L.NGA_EINVAL     # xc and yc overlap
+    assert call(ws=None) == L.NGA_EWORKSPACE
+    assert call(wsb=8) == L.NGA_EWORKSPACE
+    assert call(nc=0) == L.NGA_OK                    # nothing to do
+    b1 = lib.local_attn_workspace_bytes(L.NGA_F32, 1000, 64, 4, 1)
+    assert b1 >= 4 * (2 * 1000 * 256 + 2 * 256 * 64)
+    assert lib.local_attn_workspace_bytes(L.NGA_F32, 1000, 64, 4, 2) >= b1 + 4 * 1000 * 64
+    assert lib.local_attn_workspace_bytes(L.NGA_F64, 1000, 256, 32, 1) == 0  # 32 heads
+
+
 def test_attention_workspace_and_variant_queries():
     lib = nga.load()
     assert lib.block_attn_workspace_bytes(9, 10, 8, 8, 2, 1) == 0
