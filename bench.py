@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--local-atten", action="store_true",
                     help="also time local_attn_forward (LocalAtten: one query per centre over "
                          "its edges, random centre rows) on the same CSR and edge features")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured as one HIP graph (nga_step_graph_*) on "
+                         "the same inputs, replayed --steps times")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter scaling)")
@@ -235,6 +238,28 @@ def main():
                       ev[2].elapsed_time(ev[3])] for ev in events])
     nl_ms, csr_ms, attn_ms = (float(v) for v in part.mean(axis=0))
 
+    graph_rec = None
+    if args.graph:
+        x_cap = torch.zeros((e_cap, w.c), dtype=x.dtype, device=dev)
+        x_cap[:e] = x
+        g = nga.StepGraph(pos, box, w.rcut, w.sel, x_cap, wt, w.heads)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        g.check()
+        tg0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        tg1 = time.perf_counter()
+        g.check()
+        if not torch.equal(g.y[:e], y[:e]):
+            raise RuntimeError("graph replay differs from the eager step")
+        g_ms = (tg1 - tg0) * 1e3 / args.steps
+        graph_rec = {"ms_per_step": g_ms, "atoms_per_s": n / (g_ms * 1e-3),
+                     "eager_ms_per_step": ms_step, "speedup": ms_step / g_ms}
+        del g
+
     smooth_rec = None
     if args.smooth:
         counts = np.diff(rp)
@@ -334,6 +359,8 @@ def main():
         "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
                    "frac": nl_gbs / PEAK_HBM_GBS},
     }
+    if graph_rec is not None:
+        rec["graph"] = graph_rec
     if smooth_rec is not None:
         rec["smooth"] = smooth_rec
     if local_rec is not None:

@@ -290,6 +290,38 @@ int pair_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
                       int64_t pair_chunk, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* The step as one HIP graph                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Capture one step -- nl_build, edge_csr without readback, block_attn_forward
+ * over x / y of e_cap rows in destination order -- as a HIP graph ([P1]
+ * "Proposed optimizations": capture the inference step in a graph to remove
+ * the per-kernel launch overhead).  Arguments are those of the three calls;
+ * every pointer is baked into the graph, so a replay reads the positions,
+ * features and weights those buffers hold at replay time and writes the same
+ * outputs; h_box and the other scalars are taken at capture.  Arguments are checked as the calls check them (the error code of
+ * the first failing call is returned and no graph is made).  The capture
+ * runs on a stream of its own; nothing is launched.  On success *graph_out
+ * receives an opaque handle, to be released with nga_step_graph_destroy.
+ * Creating a graph allocates host-side and runtime graph objects (no device
+ * buffers).  Replays of one graph must be ordered (they share workspaces).
+ */
+int nga_step_graph_create(const double* pos, int64_t n_atoms, const double* h_box, double rcut,
+                          int32_t sel, int32_t* nbr, int32_t* nbr_shift, int32_t* nnei,
+                          void* ws_nl, size_t ws_nl_bytes, int64_t* row_ptr, int32_t* col,
+                          int32_t* shift, int32_t* dst, double* edge_vec, int64_t e_cap,
+                          void* ws_csr, size_t ws_csr_bytes, int dtype, int32_t c,
+                          int32_t n_heads, int32_t n_layers, const void* weights, const void* x,
+                          void* y, void* ws_attn, size_t ws_attn_bytes, void** graph_out);
+
+/* Launch one replay of a captured step on `stream` (enqueue only). */
+int nga_step_graph_launch(void* graph, void* stream);
+
+/* Release a captured step (NULL is accepted). */
+int nga_step_graph_destroy(void* graph);
+
+/* ------------------------------------------------------------------------ */
 /* Status                                                                    */
 /* ------------------------------------------------------------------------ */
 

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     NGA_F64,
     ROW_CAP,
     NGAError,
+    StepGraph,
     Workspace,
     attn_variant,
     block_attn_forward,

@@ -24,7 +24,8 @@ ROW_CAP = 512
 EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "edge_csr",
            "block_attn_workspace_bytes", "block_attn_forward", "nga_sync_status", "nga_strerror",
            "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward",
-           "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward")
+           "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward",
+           "nga_step_graph_create", "nga_step_graph_launch", "nga_step_graph_destroy")
 
 
 class NGAError(RuntimeError):
@@ -62,6 +63,14 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward_smooth.restype = ctypes.c_int
     lib.block_attn_forward_smooth.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32,
                                               vp, vp, vp, vp, vp, sz, vp]
+    lib.nga_step_graph_create.restype = ctypes.c_int
+    lib.nga_step_graph_create.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, vp, sz, vp, vp, vp,
+                                          vp, vp, i64, vp, sz, ctypes.c_int, i32, i32, i32, vp,
+                                          vp, vp, vp, sz, ctypes.POINTER(vp)]
+    lib.nga_step_graph_launch.restype = ctypes.c_int
+    lib.nga_step_graph_launch.argtypes = [vp, vp]
+    lib.nga_step_graph_destroy.restype = ctypes.c_int
+    lib.nga_step_graph_destroy.argtypes = [vp]
     lib.local_attn_workspace_bytes.restype = sz
     lib.local_attn_workspace_bytes.argtypes = [ctypes.c_int, i64, i32, i32, i32]
     lib.local_attn_forward.restype = ctypes.c_int
@@ -377,3 +386,62 @@ def local_attn_forward(row_ptr: torch.Tensor, xc: torch.Tensor, x: torch.Tensor,
                                 ws.ptr(), ws.nbytes, _stream(dev))
     _check(rc, "local_attn_forward")
     return yc
+
+
+class StepGraph:
+    """One step (nl_build, edge_csr without readback, block_attn_forward) captured as a HIP
+    graph over fixed buffers; replay() launches it on the current stream.  The buffers are
+    allocated here and exposed as attributes: pos (update in place between replays), nbr,
+    nbr_shift, nnei, row_ptr, col, shift, dst, x, weights and y."""
+
+    def __init__(self, pos: torch.Tensor, box, rcut: float, sel: int, x: torch.Tensor,
+                 weights: torch.Tensor, n_heads: int):
+        lib = load()
+        dev = pos.device
+        n = pos.shape[0]
+        _need(pos, "pos", torch.float64, (n, 3), dev)
+        e_cap = n * int(sel)
+        c = x.shape[1]
+        _need(x, "x", x.dtype, (e_cap, c), dev)
+        layers = weights.shape[0]
+        _need(weights, "weights", x.dtype, (layers, 4, c, c), dev)
+        dt = _attn_dtype(x)
+        self.pos, self.x, self.weights = pos, x, weights
+        self.box = _box3(box)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.nbr = torch.empty((n, sel), **i32)
+        self.nbr_shift = torch.empty((n, sel, 3), **i32)
+        self.nnei = torch.empty((n,), **i32)
+        self.row_ptr = torch.empty((n + 1,), dtype=torch.int64, device=dev)
+        self.col = torch.empty((e_cap,), **i32)
+        self.shift = torch.empty((e_cap, 3), **i32)
+        self.dst = torch.empty((e_cap,), **i32)
+        self.y = torch.empty_like(x)
+        self.ws_nl = Workspace(dev, nl_build_workspace_bytes(n, box, rcut))
+        self.ws_csr = Workspace(dev, int(lib.edge_csr_workspace_bytes(n, int(sel))))
+        self.ws_attn = Workspace(dev, block_attn_workspace_bytes(dt, e_cap, sel, c, n_heads,
+                                                                 layers))
+        handle = ctypes.c_void_p()
+        rc = lib.nga_step_graph_create(
+            _ptr(pos), n, self.box, float(rcut), int(sel), _ptr(self.nbr), _ptr(self.nbr_shift),
+            _ptr(self.nnei), self.ws_nl.ptr(), self.ws_nl.nbytes, _ptr(self.row_ptr),
+            _ptr(self.col), _ptr(self.shift), _ptr(self.dst), None, e_cap, self.ws_csr.ptr(),
+            self.ws_csr.nbytes, dt, c, int(n_heads), int(layers), _ptr(weights), _ptr(x),
+            _ptr(self.y), self.ws_attn.ptr(), self.ws_attn.nbytes, ctypes.byref(handle))
+        _check(rc, "nga_step_graph_create")
+        self._lib, self._handle, self._dev = lib, handle, dev
+
+    def replay(self) -> None:
+        _check(self._lib.nga_step_graph_launch(self._handle, _stream(self._dev)),
+               "nga_step_graph_launch")
+
+    def check(self) -> None:
+        """Synchronise and raise on any device-detected error of the replays so far."""
+        for ws, name in ((self.ws_nl, "nl_build"), (self.ws_csr, "edge_csr"),
+                         (self.ws_attn, "block_attn_forward")):
+            check_status(ws, name)
+
+    def __del__(self):
+        if getattr(self, "_handle", None):
+            self._lib.nga_step_graph_destroy(self._handle)
+            self._handle = None
