@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured as one HIP graph (nga_step_graph_*) on "
                          "the same inputs, replayed --steps times")
+    ap.add_argument("--nl-reuse", action="store_true",
+                    help="also time neighbour-list reuse: candidate rows at rcut + skin once, "
+                         "then nl_refine and nl_max_displacement per step")
+    ap.add_argument("--skin", type=float, default=1.0)
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter scaling)")
@@ -238,6 +242,43 @@ def main():
                       ev[2].elapsed_time(ev[3])] for ev in events])
     nl_ms, csr_ms, attn_ms = (float(v) for v in part.mean(axis=0))
 
+    reuse_rec = None
+    if args.nl_reuse:
+        cand_sel = 512
+        ws_cand = nga.Workspace(dev, nga.nl_build_workspace_bytes(n, box, w.rcut + args.skin))
+        ws_ref = nga.Workspace(dev)
+        cands = nga.nl_build(pos, box, w.rcut + args.skin, cand_sel, ws=ws_cand)
+        nga.check_status(ws_cand, "nl_build (candidates)")
+        if int(cands[2].max().item()) >= cand_sel:
+            raise RuntimeError("candidate rows reach their capacity; lower --skin")
+        dmax = torch.empty((1,), dtype=torch.float64, device=dev)
+        pos_ref = pos.clone()
+
+        def timed(fn, k):
+            for _ in range(args.warmup):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(k)]
+            for e0, e1 in evs:
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize(dev)
+            return float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+        cand_ms = timed(lambda: nga.nl_build(pos, box, w.rcut + args.skin, cand_sel, nbr=cands[0],
+                                             nbr_shift=cands[1], nnei=cands[2], ws=ws_cand),
+                        max(3, args.steps // 5))
+        refine_ms = timed(lambda: nga.nl_refine(pos, box, w.rcut, w.sel, cands[0], cands[1],
+                                                cands[2], box, nbr=nbr, nbr_shift=nbr_shift,
+                                                nnei=nnei, ws=ws_ref), args.steps)
+        disp_ms = timed(lambda: nga.nl_max_displacement(pos, pos_ref, box, out=dmax), args.steps)
+        nga.check_status(ws_ref, "nl_refine")
+        reuse_rec = {"skin": args.skin, "candidate_rows": cand_sel,
+                     "candidate_build_ms": cand_ms, "refine_ms": refine_ms,
+                     "max_displacement_ms": disp_ms, "nl_build_ms": nl_ms,
+                     "refine_vs_build": refine_ms / nl_ms}
+
     graph_rec = None
     if args.graph:
         x_cap = torch.zeros((e_cap, w.c), dtype=x.dtype, device=dev)
@@ -361,6 +402,8 @@ def main():
     }
     if graph_rec is not None:
         rec["graph"] = graph_rec
+    if reuse_rec is not None:
+        rec["nl_reuse"] = reuse_rec
     if smooth_rec is not None:
         rec["smooth"] = smooth_rec
     if local_rec is not None:

@@ -5,6 +5,7 @@
  * one MI355X (gfx950) GPU:
  *
  *   nl_build            O(N) cell-list neighbour rows under periodic boundaries
+ *   nl_refine           the same rows from cached candidate rows (reuse)
  *   edge_csr            those rows as a destination CSR with image shifts
  *   block_attn_forward  block-dense multi-head attention through the CSR
  *   block_attn_forward_smooth  the same with a per-segment softmax rescale
@@ -105,6 +106,42 @@ size_t nl_build_workspace_bytes(int64_t n_atoms, const double* h_box, double rcu
 int nl_build(const double* pos, int64_t n_atoms, const double* h_box, double rcut, int32_t sel,
              int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, size_t ws_bytes,
              void* stream);
+
+/*
+ * Neighbour rows of the current positions from candidate rows built earlier
+ * by nl_build with a larger cutoff rcut + skin ([P1] "Proposed
+ * optimizations": when ago > 0 -- neighbour list unchanged -- reuse what was
+ * built instead of rebuilding it).  Each candidate (j, shift) of centre i is
+ * re-evaluated with the pinned distance formula at `pos`, those within rcut
+ * are kept and ranked by the same total key as nl_build, and the first
+ * min(sel, count) are written as rows in nl_build's layout.  The result is
+ * bit-identical to nl_build(pos, rcut, sel) as long as the candidate rows
+ * hold every pair within rcut: true when no atom has moved more than skin / 2
+ * since the candidates were built (see nl_max_displacement) and no candidate
+ * row was cut at cand_sel (choose cand_sel above the largest count within
+ * rcut + skin).  Positions must move continuously between a candidate build
+ * and its refines (not re-wrapped into the box: the stored image shifts
+ * assume the candidate-time images).
+ *
+ * cand_nbr, cand_shift, cand_nnei   nl_build's rows [N][cand_sel] (nnei
+ *                                   nullable: rows end at the first -1).
+ * cand_sel      <= NGA_ROW_CAP.
+ * h_cand_box    the box the candidates were built in; a different h_box
+ *               returns NGA_EINVAL (the cached rows belong to another cell).
+ * ws            needs only its 256-byte header.
+ * Device-detected: NGA_EINDEX (a candidate index or shift out of range).
+ */
+int nl_refine(const double* pos, int64_t n_atoms, const double* h_box, double rcut, int32_t sel,
+              const int32_t* cand_nbr, const int32_t* cand_shift, const int32_t* cand_nnei,
+              int32_t cand_sel, const double* h_cand_box, int32_t* nbr, int32_t* nbr_shift,
+              int32_t* nnei, void* ws, size_t ws_bytes, void* stream);
+
+/* The largest displacement |pos_i - pos_ref_i| (minimum image per axis) over
+ * the atoms, written to the device double *d_max (set to 0 first; enqueued on
+ * `stream`, no host synchronisation): the test for reusing candidate rows,
+ * d_max < skin / 2. */
+int nl_max_displacement(const double* pos, const double* pos_ref, int64_t n_atoms,
+                        const double* h_box, double* d_max, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Destination CSR                                                           */

@@ -30,6 +30,8 @@ from ._lib import (  # noqa: F401
     nl_build,
     local_attn_forward,
     nl_build_workspace_bytes,
+    nl_max_displacement,
+    nl_refine,
     pair_attn_forward,
     pair_attn_workspace_bytes,
     strerror,

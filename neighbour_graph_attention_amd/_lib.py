@@ -25,7 +25,8 @@ EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "
            "block_attn_workspace_bytes", "block_attn_forward", "nga_sync_status", "nga_strerror",
            "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward",
            "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward",
-           "nga_step_graph_create", "nga_step_graph_launch", "nga_step_graph_destroy")
+           "nga_step_graph_create", "nga_step_graph_launch", "nga_step_graph_destroy",
+           "nl_refine", "nl_max_displacement")
 
 
 class NGAError(RuntimeError):
@@ -63,6 +64,10 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward_smooth.restype = ctypes.c_int
     lib.block_attn_forward_smooth.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32,
                                               vp, vp, vp, vp, vp, sz, vp]
+    lib.nl_refine.restype = ctypes.c_int
+    lib.nl_refine.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.nl_max_displacement.restype = ctypes.c_int
+    lib.nl_max_displacement.argtypes = [vp, vp, i64, vp, vp, vp]
     lib.nga_step_graph_create.restype = ctypes.c_int
     lib.nga_step_graph_create.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, vp, sz, vp, vp, vp,
                                           vp, vp, i64, vp, sz, ctypes.c_int, i32, i32, i32, vp,
@@ -445,3 +450,48 @@ class StepGraph:
         if getattr(self, "_handle", None):
             self._lib.nga_step_graph_destroy(self._handle)
             self._handle = None
+
+
+def nl_refine(pos: torch.Tensor, box, rcut: float, sel: int, cand_nbr: torch.Tensor,
+              cand_shift: torch.Tensor, cand_nnei: torch.Tensor | None, cand_box, *, nbr=None,
+              nbr_shift=None, nnei=None, ws: Workspace | None = None):
+    """Neighbour rows at pos from candidate rows built by nl_build with rcut + skin in the box
+    cand_box; returns (nbr [N][sel], nbr_shift [N][sel][3], nnei [N])."""
+    lib = load()
+    dev = pos.device
+    n = pos.shape[0]
+    _need(pos, "pos", torch.float64, (n, 3), dev)
+    csel = cand_nbr.shape[1] if cand_nbr.dim() == 2 else -1
+    _need(cand_nbr, "cand_nbr", torch.int32, (n, csel), dev)
+    _need(cand_shift, "cand_shift", torch.int32, (n, csel, 3), dev)
+    if cand_nnei is not None:
+        _need(cand_nnei, "cand_nnei", torch.int32, (n,), dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    nbr = torch.empty((n, sel), **i32) if nbr is None else nbr
+    nbr_shift = torch.empty((n, sel, 3), **i32) if nbr_shift is None else nbr_shift
+    nnei = torch.empty((n,), **i32) if nnei is None else nnei
+    _need(nbr, "nbr", torch.int32, (n, sel), dev)
+    _need(nbr_shift, "nbr_shift", torch.int32, (n, sel, 3), dev)
+    _need(nnei, "nnei", torch.int32, (n,), dev)
+    ws = _ws(ws, dev, 256)
+    rc = lib.nl_refine(_ptr(pos), n, _box3(box), float(rcut), int(sel), _ptr(cand_nbr),
+                       _ptr(cand_shift), _ptr(cand_nnei), int(csel), _box3(cand_box), _ptr(nbr),
+                       _ptr(nbr_shift), _ptr(nnei), ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "nl_refine")
+    return nbr, nbr_shift, nnei
+
+
+def nl_max_displacement(pos: torch.Tensor, pos_ref: torch.Tensor, box,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """Largest minimum-image displacement between pos and pos_ref, as a 1-element device
+    tensor (no synchronisation)."""
+    lib = load()
+    dev = pos.device
+    n = pos.shape[0]
+    _need(pos, "pos", torch.float64, (n, 3), dev)
+    _need(pos_ref, "pos_ref", torch.float64, (n, 3), dev)
+    out = torch.empty((1,), dtype=torch.float64, device=dev) if out is None else out
+    _need(out, "out", torch.float64, (1,), dev)
+    _check(lib.nl_max_displacement(_ptr(pos), _ptr(pos_ref), n, _box3(box), _ptr(out),
+                                   _stream(dev)), "nl_max_displacement")
+    return out

@@ -501,9 +501,170 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     return last_launch_status();
 }
 
+// ---------------------------------------------------------------------------------------
+// Reuse across steps ("ago > 0" in deepmd-kit issue "perf: DPA4 .pt2 LAMMPS (C++ AOTI)
+// inference 3-6x slower ...", section "Proposed optimizations": keep what was built while
+// the neighbour list is unchanged).  Candidate rows built once with a larger cutoff
+// rcut + skin hold, while no atom has moved more than skin / 2, every pair within rcut; the
+// rows of the current positions are then the candidates re-evaluated and re-ranked.
+
+struct RefineArgs {
+    const double* pos;
+    int n;
+    double L[3];
+    double rc2;
+    int sel;
+    const int32_t* cnbr;
+    const int32_t* cshift;
+    const int32_t* cnnei;
+    int csel;
+    int32_t* nbr;
+    int32_t* nbr_shift;
+    int32_t* nnei;
+    uint32_t* status;
+};
+
+// One wavefront per centre: the pinned fp64 distance of each candidate at the current
+// positions, those within rcut compacted into the wave's LDS list with ballot / mbcnt, then
+// the same ranking and row write as nl_build (sort_and_write), so that the row equals the one
+// nl_build makes from the same positions whenever the candidates hold every pair within rcut.
+__global__ void __launch_bounds__(kNlBlock) refine_kernel(RefineArgs A) {
+    __shared__ WaveList lists[kNlWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int i = blockIdx.x * kNlWaves + wave;
+    if (i >= A.n) return;  // whole wavefronts; the kernel has no work-group barrier
+    WaveList& L = lists[wave];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const double xi = A.pos[3 * (int64_t)i], yi = A.pos[3 * (int64_t)i + 1],
+                 zi = A.pos[3 * (int64_t)i + 2];
+    int cn = A.cnnei ? A.cnnei[i] : A.csel;
+    cn = cn < 0 ? 0 : (cn > A.csel ? A.csel : cn);
+    const int32_t* crow = A.cnbr + (int64_t)i * A.csel;
+    const int32_t* csh = A.cshift + (int64_t)i * A.csel * 3;
+    bool bad = false;
+    int count = 0;
+    for (int t0 = 0; t0 < cn; t0 += 64) {
+        const int t = t0 + lane;
+        bool accept = false;
+        double r2 = 0.0;
+        int j = 0, code = 0;
+        if (t < cn) {
+            j = crow[t];
+            const int nx = csh[3 * t], ny = csh[3 * t + 1], nz = csh[3 * t + 2];
+            if (j >= 0 && j < A.n && nx >= -127 && nx <= 127 && ny >= -127 && ny <= 127 &&
+                nz >= -127 && nz <= 127) {
+                const double dx = (A.pos[3 * (int64_t)j] - xi) + (double)nx * A.L[0];
+                const double dy = (A.pos[3 * (int64_t)j + 1] - yi) + (double)ny * A.L[1];
+                const double dz = (A.pos[3 * (int64_t)j + 2] - zi) + (double)nz * A.L[2];
+                const double sxy = dx * dx + dy * dy;
+                r2 = sxy + dz * dz;
+                accept = r2 < A.rc2 && !(j == i && nx == 0 && ny == 0 && nz == 0);
+                code = pack_shift(nx, ny, nz);
+            } else if (j >= 0) {
+                bad = true;
+            }
+        }
+        const uint64_t m = __ballot(accept);
+        const int slot = count + __popcll(m & lt_mask);
+        if (accept) {
+            L.r2[slot] = (uint64_t)__double_as_longlong(r2);
+            L.j[slot] = j;
+            L.code[slot] = code;
+        }
+        count += __popcll(m);
+    }
+    wave_sync_lds();
+    const int keep = count < A.sel ? count : A.sel;
+    int32_t* row = A.nbr + (int64_t)i * A.sel;
+    int32_t* rsh = A.nbr_shift + (int64_t)i * A.sel * 3;
+    if (count <= 64) sort_and_write<1>(L, count, keep, A.sel, row, rsh, lane);
+    else if (count <= 128) sort_and_write<2>(L, count, keep, A.sel, row, rsh, lane);
+    else if (count <= 256) sort_and_write<4>(L, count, keep, A.sel, row, rsh, lane);
+    else sort_and_write<8>(L, count, keep, A.sel, row, rsh, lane);
+    if (lane == 0) A.nnei[i] = keep;
+    if (__ballot(bad) && lane == 0) raise_bits(A.status, kBitIndex);
+}
+
+__global__ void zero_f64_kernel(double* p) { *p = 0.0; }
+
+// max over atoms of |pos - pos_ref| (minimum image per axis), via an atomic max on the bit
+// patterns (non-negative doubles order as their signed 64-bit patterns).
+__global__ void __launch_bounds__(256)
+max_displacement_kernel(const double* __restrict__ pos, const double* __restrict__ ref, int n,
+                        double Lx, double Ly, double Lz, double* out) {
+    double m = 0.0;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+        double dx = pos[3 * (int64_t)i] - ref[3 * (int64_t)i];
+        double dy = pos[3 * (int64_t)i + 1] - ref[3 * (int64_t)i + 1];
+        double dz = pos[3 * (int64_t)i + 2] - ref[3 * (int64_t)i + 2];
+        dx -= Lx * rint(dx / Lx);
+        dy -= Ly * rint(dy / Ly);
+        dz -= Lz * rint(dz / Lz);
+        const double d = sqrt((dx * dx + dy * dy) + dz * dz);
+        m = d > m ? d : m;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const double o = __shfl_xor(m, off, 64);
+        m = o > m ? o : m;
+    }
+    if ((threadIdx.x & 63) == 0 && m > 0.0)
+        atomicMax(reinterpret_cast<unsigned long long*>(out),
+                  (unsigned long long)__double_as_longlong(m));
+}
+
 }  // namespace
 
 }  // namespace nga
+
+extern "C" int nl_refine(const double* pos, int64_t n_atoms, const double* h_box, double rcut,
+                         int32_t sel, const int32_t* cand_nbr, const int32_t* cand_shift,
+                         const int32_t* cand_nnei, int32_t cand_sel, const double* h_cand_box,
+                         int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws,
+                         size_t ws_bytes, void* stream) {
+    using namespace nga;
+    if (n_atoms < 0 || n_atoms >= INT32_MAX || !h_box || !h_cand_box || !(rcut > 0.0) ||
+        !std::isfinite(rcut))
+        return NGA_EINVAL;
+    for (int a = 0; a < 3; ++a) {
+        if (!finite_pos(h_box[a])) return NGA_EINVAL;
+        if (h_cand_box[a] != h_box[a]) return NGA_EINVAL;  // candidates of another box: stale
+    }
+    if (sel < 1 || cand_sel < 1 || cand_sel > NGA_ROW_CAP) return NGA_EINVAL;
+    if (n_atoms == 0) return NGA_OK;
+    if (!pos || !cand_nbr || !cand_shift || !nbr || !nbr_shift || !nnei) return NGA_EINVAL;
+    if (!ws || ws_bytes < sizeof(WsHeader)) return NGA_EWORKSPACE;
+    RefineArgs A;
+    A.pos = pos;
+    A.n = (int)n_atoms;
+    A.L[0] = h_box[0]; A.L[1] = h_box[1]; A.L[2] = h_box[2];
+    A.rc2 = rcut * rcut;
+    A.sel = sel;
+    A.cnbr = cand_nbr; A.cshift = cand_shift; A.cnnei = cand_nnei; A.csel = cand_sel;
+    A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
+    A.status = &static_cast<WsHeader*>(ws)->status;
+    const unsigned blocks = (unsigned)((n_atoms + kNlWaves - 1) / kNlWaves);
+    hipLaunchKernelGGL(refine_kernel, dim3(blocks), dim3(kNlBlock), 0,
+                       static_cast<hipStream_t>(stream), A);
+    return last_launch_status();
+}
+
+extern "C" int nl_max_displacement(const double* pos, const double* pos_ref, int64_t n_atoms,
+                                   const double* h_box, double* d_max, void* stream) {
+    using namespace nga;
+    if (n_atoms < 0 || n_atoms >= INT32_MAX || !h_box || !d_max) return NGA_EINVAL;
+    for (int a = 0; a < 3; ++a)
+        if (!finite_pos(h_box[a])) return NGA_EINVAL;
+    if (n_atoms > 0 && (!pos || !pos_ref)) return NGA_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(zero_f64_kernel, dim3(1), dim3(1), 0, s, d_max);
+    if (n_atoms > 0) {
+        int64_t blocks = (n_atoms + 255) / 256;
+        if (blocks > 1024) blocks = 1024;
+        hipLaunchKernelGGL(max_displacement_kernel, dim3((unsigned)blocks), dim3(256), 0, s, pos,
+                           pos_ref, (int)n_atoms, h_box[0], h_box[1], h_box[2], d_max);
+    }
+    return last_launch_status();
+}
 
 extern "C" size_t nl_build_workspace_bytes(int64_t n_atoms, const double* h_box, double rcut) {
     nga::Geom g;

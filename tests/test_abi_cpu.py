@@ -181,6 +181,29 @@ def test_local_attn_rejects_bad_arguments():
     assert lib.local_attn_workspace_bytes(L.NGA_F64, 1000, 256, 32, 1) == 0  # 32 heads
 
 
+def test_nl_refine_and_displacement_reject_bad_arguments():
+    lib = nga.load()
+    box = (ctypes.c_double * 3)(5.0, 5.0, 5.0)
+    other = (ctypes.c_double * 3)(5.0, 5.0, 5.5)
+
+    def call(n=10, rcut=2.0, sel=8, csel=16, cbox=box, ws=FAKE, wsb=256, rp=FAKE):
+        return lib.nl_refine(rp, n, box, rcut, sel, FAKE, FAKE, None, csel, cbox, FAKE, FAKE,
+                             FAKE, ws, wsb, None)
+
+    assert call(rcut=0.0) == L.NGA_EINVAL
+    assert call(sel=0) == L.NGA_EINVAL
+    assert call(csel=0) == L.NGA_EINVAL
+    assert call(csel=L.ROW_CAP + 1) == L.NGA_EINVAL
+    assert call(cbox=other) == L.NGA_EINVAL          # candidates of another box
+    assert call(cbox=None) == L.NGA_EINVAL
+    assert call(rp=None) == L.NGA_EINVAL
+    assert call(ws=None) == L.NGA_EWORKSPACE
+    assert call(wsb=8) == L.NGA_EWORKSPACE
+    assert call(n=0) == L.NGA_OK
+    assert lib.nl_max_displacement(FAKE, FAKE, 10, box, None, None) == L.NGA_EINVAL
+    assert lib.nl_max_displacement(None, FAKE, 10, box, FAKE, None) == L.NGA_EINVAL
+
+
 def test_attention_workspace_and_variant_queries():
     lib = nga.load()
     assert lib.block_attn_workspace_bytes(9, 10, 8, 8, 2, 1) == 0

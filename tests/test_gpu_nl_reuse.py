@@ -1,0 +1,93 @@
+"""Neighbour-list reuse across steps (nl_refine, nl_max_displacement) against nl_build.
+
+Candidate rows are built once with rcut + skin; the atoms then take several steps, each within
+skin / 2 of the candidate-time positions and inside the box, and every refined row set must
+equal nl_build's rows at the same positions bit for bit (indices, shifts, counts).  Workloads
+with several images per pair (rcut + skin beyond half the box), the Fe workloads at full size,
+a tiny random box; the displacement query against numpy; the stale-box guard and bad indices.
+"""
+import numpy as np
+import pytest
+import torch
+
+import neighbour_graph_attention_amd as nga
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def _steps(pos0, box, skin, seed, n_steps=3):
+    """Positions within skin/2 of pos0 (each atom), inside [0, L), after each of n_steps."""
+    rng = np.random.default_rng(seed)
+    box = np.asarray(box)
+    out = []
+    for k in range(n_steps):
+        d = rng.normal(0.0, 0.04 * (k + 1), pos0.shape)
+        norm = np.linalg.norm(d, axis=1, keepdims=True)
+        d = np.where(norm > 0.49 * skin, d * (0.49 * skin / np.maximum(norm, 1e-300)), d)
+        p = pos0 + d
+        inside = np.all((p >= 0.0) & (p < box), axis=1, keepdims=True)
+        out.append(np.where(inside, p, pos0))
+    return out
+
+
+def _check_case(pos0, box, rcut, sel, skin, seed):
+    cand_sel = 512
+    p0 = torch.from_numpy(pos0).to(DEV)
+    cn, cs, cnn = nga.nl_build(p0, box, rcut + skin, cand_sel)
+    assert int(cnn.max().item()) < cand_sel  # no candidate row was cut
+    for k, pk in enumerate(_steps(pos0, box, skin, seed)):
+        p = torch.from_numpy(pk).to(DEV)
+        dmax = float(nga.nl_max_displacement(p, p0, box).item())
+        assert dmax < skin / 2
+        ws = nga.Workspace(DEV)
+        nbr, nsh, nn = nga.nl_refine(p, box, rcut, sel, cn, cs, cnn, box, ws=ws)
+        nga.check_status(ws, "nl_refine")
+        rb, rs, rn = nga.nl_build(p, box, rcut, sel)
+        print(f"step {k}: max displacement {dmax:.3f}, edges {int(rn.sum().item())}", flush=True)
+        assert torch.equal(nn, rn)
+        assert torch.equal(nbr, rb)
+        assert torch.equal(nsh, rs)
+
+
+@pytest.mark.parametrize("key,skin", [(2, 1.0), (3, 1.0), (4, 1.0), (5, 1.0)])
+def test_refine_equals_rebuild_on_workloads(key, skin):
+    w = W.WORKLOADS[key]
+    pos, box = W.workload_positions(w)
+    print(f"workload {w.name} rcut {w.rcut} skin {skin}", flush=True)
+    _check_case(pos, box, w.rcut, w.sel, skin, 900 + key)
+
+
+def test_refine_equals_rebuild_tiny_box():
+    box = (4.0, 5.0, 6.0)
+    pos = W.random_positions(40, box, 901)
+    _check_case(pos, box, 3.5, 200, 0.6, 902)
+
+
+def test_max_displacement_matches_minimum_image():
+    box = np.array([9.0, 10.0, 11.0])
+    rng = np.random.default_rng(903)
+    a = rng.uniform(0, 1, (1000, 3)) * box
+    b = a + rng.normal(0, 0.3, a.shape)
+    b[::7] += box * np.array([1.0, 0.0, -1.0])  # whole-box jumps are no displacement
+    d = b - a
+    d -= box * np.rint(d / box)
+    ref = float(np.max(np.linalg.norm(d, axis=1)))
+    got = float(nga.nl_max_displacement(torch.from_numpy(b).to(DEV),
+                                        torch.from_numpy(a).to(DEV), box).item())
+    assert abs(got - ref) <= 1e-12 * ref
+
+
+def test_stale_box_and_bad_candidates():
+    box = (6.0, 6.0, 6.0)
+    pos = torch.from_numpy(W.random_positions(30, box, 904)).to(DEV)
+    cn, cs, cnn = nga.nl_build(pos, box, 3.0, 64)
+    with pytest.raises(nga.NGAError):
+        nga.nl_refine(pos, box, 2.5, 32, cn, cs, cnn, (6.0, 6.0, 6.5))  # candidates of another box
+    bad = cn.clone()
+    bad[3, 0] = 1000  # index beyond the atoms
+    ws = nga.Workspace(DEV)
+    nga.nl_refine(pos, box, 2.5, 32, bad, cs, cnn, box, ws=ws)
+    assert nga.sync_status(ws) == -8
