@@ -49,8 +49,13 @@ struct CoreArgs {
     uint32_t* status;
 };
 
-// One work-group per centre; each thread owns (query row a, head h) pairs and makes two
-// passes over the centre's keys: the row max, then exp / sum / weighted values.
+// One work-group per centre; each thread owns (query row a, head h) pairs and streams the
+// centre's keys once, in tiles of kCoreKeys, with the online-softmax recurrence ([P2]
+// "Graph-native alternatives": a running max and denominator over bounded tiles, memory
+// O(E c)): per tile the scores, the tile max, a rescale of the running sum and weighted
+// values when the max grows, then exp / sum / weighted values.  Rows of any length.
+constexpr int kCoreKeys = 16;
+
 template <typename T, int DMAX>
 __global__ void __launch_bounds__(256) attn_core_kernel(CoreArgs<T> A) {
     const int i = blockIdx.x;
@@ -67,33 +72,46 @@ __global__ void __launch_bounds__(256) attn_core_kernel(CoreArgs<T> A) {
         const T* q = A.qkv + (r0 + a) * c3 + h * d;
         T qr[DMAX];
 #pragma unroll
-        for (int t = 0; t < DMAX; ++t) qr[t] = t < d ? q[t] : T(0);
-        T m = -INFINITY;
-        for (int b = 0; b < n; ++b) {
-            const T* kb = A.qkv + (r0 + b) * c3 + c + h * d;
-            T s = T(0);
-#pragma unroll
-            for (int t = 0; t < DMAX; ++t)
-                if (t < d) s += qr[t] * kb[t];
-            s *= A.scale;
-            m = s > m ? s : m;
-        }
+        for (int t = 0; t < DMAX; ++t) qr[t] = t < d ? q[t] * A.scale : T(0);
+        T m = -INFINITY, z = T(0);
         T acc[DMAX];
 #pragma unroll
         for (int t = 0; t < DMAX; ++t) acc[t] = T(0);
-        T z = T(0);
-        for (int b = 0; b < n; ++b) {
-            const T* kb = A.qkv + (r0 + b) * c3 + c + h * d;
-            const T* vb = A.qkv + (r0 + b) * c3 + 2 * c + h * d;
-            T s = T(0);
+        for (int b0 = 0; b0 < n; b0 += kCoreKeys) {
+            const int nb = n - b0 < kCoreKeys ? n - b0 : kCoreKeys;
+            T s[kCoreKeys];
+            T mt = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < DMAX; ++t)
-                if (t < d) s += qr[t] * kb[t];
-            const T p = exp_t<T>(s * A.scale - m);
-            z += p;
+            for (int k = 0; k < kCoreKeys; ++k) {
+                s[k] = -INFINITY;
+                if (k < nb) {
+                    const T* kb = A.qkv + (r0 + b0 + k) * c3 + c + h * d;
+                    T v = T(0);
 #pragma unroll
-            for (int t = 0; t < DMAX; ++t)
-                if (t < d) acc[t] += p * vb[t];
+                    for (int t = 0; t < DMAX; ++t)
+                        if (t < d) v += qr[t] * kb[t];
+                    s[k] = v;
+                    mt = v > mt ? v : mt;
+                }
+            }
+            if (mt > m) {  // the running max grows: rescale what was summed so far
+                const T alpha = exp_t<T>(m - mt);  // 0 for the first tile
+                z *= alpha;
+#pragma unroll
+                for (int t = 0; t < DMAX; ++t) acc[t] *= alpha;
+                m = mt;
+            }
+#pragma unroll
+            for (int k = 0; k < kCoreKeys; ++k) {
+                if (k < nb) {
+                    const T* vb = A.qkv + (r0 + b0 + k) * c3 + 2 * c + h * d;
+                    const T p = exp_t<T>(s[k] - m);
+                    z += p;
+#pragma unroll
+                    for (int t = 0; t < DMAX; ++t)
+                        if (t < d) acc[t] += p * vb[t];
+                }
+            }
         }
         T* out = A.o + (r0 + a) * c + h * d;
         // Smooth attention: sum_j e_j / D~ times the softmax = exp(s_j - ln D~), i.e. the

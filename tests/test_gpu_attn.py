@@ -97,6 +97,9 @@ CASES = [
     (np.float32, 40, 96, 32, 2, 1, 8),
     (np.float32, 25, 50, 48, 3, 2, 9),
     (np.float32, 30, 20, 16, 1, 1, 10),
+    (np.float32, 20, 400, 64, 4, 2, 15),     # rows past 192: generic online-softmax path
+    (np.float32, 10, 512, 16, 1, 1, 16),     # rows at the 512-neighbour cap
+    (np.float64, 15, 300, 32, 4, 1, 17),     # fp64 rows past 128: generic path
 ]
 
 
