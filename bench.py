@@ -63,6 +63,9 @@ def parse():
                     help="also time neighbour-list reuse: candidate rows at rcut + skin once, "
                          "then nl_refine and nl_max_displacement per step")
     ap.add_argument("--skin", type=float, default=1.0)
+    ap.add_argument("--nl-batch", type=int, default=0,
+                    help="also time nl_build_batch over this many jittered copies of the "
+                         "workload's structure against as many separate nl_build calls")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB "
                          "(reference kernel for HBM counter scaling)")
@@ -242,6 +245,51 @@ def main():
                       ev[2].elapsed_time(ev[3])] for ev in events])
     nl_ms, csr_ms, attn_ms = (float(v) for v in part.mean(axis=0))
 
+    batch_rec = None
+    if args.nl_batch > 0:
+        nb = args.nl_batch
+        rng_b = np.random.default_rng(800)
+        copies = [W.wrap_into_box(pos_np + rng_b.normal(0.0, 0.02, pos_np.shape), box)
+                  for _ in range(nb)]
+        pos_b = torch.from_numpy(np.concatenate(copies)).to(dev)
+        atom_ptr = [k * n for k in range(nb + 1)]
+        boxes = [box] * nb
+        ws_b = nga.Workspace(dev)
+        nbr_b = torch.empty((nb * n, w.sel), dtype=torch.int32, device=dev)
+        nsh_b = torch.empty((nb * n, w.sel, 3), dtype=torch.int32, device=dev)
+        nn_b = torch.empty((nb * n,), dtype=torch.int32, device=dev)
+        singles = [torch.from_numpy(cp).to(dev) for cp in copies]
+        ws_s = [nga.Workspace(dev, nga.nl_build_workspace_bytes(n, box, w.rcut)) for _ in range(nb)]
+        out_s = [(nbr_b[k * n:(k + 1) * n], nsh_b[k * n:(k + 1) * n], nn_b[k * n:(k + 1) * n])
+                 for k in range(nb)]
+
+        def batched():
+            nga.nl_build_batch(pos_b, atom_ptr, boxes, w.rcut, w.sel, nbr=nbr_b, nbr_shift=nsh_b,
+                               nnei=nn_b, ws=ws_b)
+
+        def separate():
+            for k in range(nb):
+                nga.nl_build(singles[k], box, w.rcut, w.sel, nbr=out_s[k][0], nbr_shift=out_s[k][1],
+                             nnei=out_s[k][2], ws=ws_s[k])
+
+        def wall(fn, k):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize(dev)
+            t0b = time.perf_counter()
+            for _ in range(k):
+                fn()
+            torch.cuda.synchronize(dev)
+            return (time.perf_counter() - t0b) * 1e3 / k
+
+        kb = max(3, args.steps // 5)
+        b_ms, s_ms = wall(batched, kb), wall(separate, kb)
+        nga.check_status(ws_b, "nl_build_batch")
+        batch_rec = {"structures": nb, "atoms_each": n, "batched_ms": b_ms,
+                     "separate_ms": s_ms, "speedup": s_ms / b_ms,
+                     "note": "wall time per call sequence; the batched call synchronises once "
+                             "to upload its structure table"}
+
     reuse_rec = None
     if args.nl_reuse:
         cand_sel = 512
@@ -404,6 +452,8 @@ def main():
         rec["graph"] = graph_rec
     if reuse_rec is not None:
         rec["nl_reuse"] = reuse_rec
+    if batch_rec is not None:
+        rec["nl_batch"] = batch_rec
     if smooth_rec is not None:
         rec["smooth"] = smooth_rec
     if local_rec is not None:

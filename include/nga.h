@@ -6,6 +6,7 @@
  *
  *   nl_build            O(N) cell-list neighbour rows under periodic boundaries
  *   nl_refine           the same rows from cached candidate rows (reuse)
+ *   nl_build_batch      neighbour rows of many structures in one launch sequence
  *   edge_csr            those rows as a destination CSR with image shifts
  *   block_attn_forward  block-dense multi-head attention through the CSR
  *   block_attn_forward_smooth  the same with a per-segment softmax rescale
@@ -106,6 +107,29 @@ size_t nl_build_workspace_bytes(int64_t n_atoms, const double* h_box, double rcu
 int nl_build(const double* pos, int64_t n_atoms, const double* h_box, double rcut, int32_t sel,
              int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, size_t ws_bytes,
              void* stream);
+
+/* Workspace bytes nl_build_batch needs (0 if the structures are invalid). */
+size_t nl_build_batch_workspace_bytes(int32_t n_structs, const int64_t* h_atom_ptr,
+                                      const double* h_boxes, double rcut);
+
+/*
+ * Neighbour rows of a batch of independent periodic structures in one launch
+ * sequence ([P4] "Goal": batched inference over many structures at once).
+ * Structure b holds atoms h_atom_ptr[b] .. h_atom_ptr[b+1]-1 of pos (all
+ * structures' positions concatenated, [N][3], N = h_atom_ptr[n_structs]) in
+ * the box h_boxes[3b .. 3b+2].  Its rows name neighbours of the same
+ * structure by their index in the concatenated arrays, with image shifts in
+ * its own box; the rows of structure b equal nl_build on that structure alone
+ * with the indices offset by h_atom_ptr[b].  Outputs as nl_build over N atoms,
+ * so edge_csr and the attention calls take the batch as one system.
+ * h_atom_ptr [n_structs + 1] (h_atom_ptr[0] = 0, non-decreasing) and h_boxes
+ * are host arrays; every structure obeys nl_build's box rules.  The call
+ * uploads a small per-structure table into the workspace and synchronises
+ * `stream` once (it is not graph-capturable).
+ */
+int nl_build_batch(const double* pos, int32_t n_structs, const int64_t* h_atom_ptr,
+                   const double* h_boxes, double rcut, int32_t sel, int32_t* nbr,
+                   int32_t* nbr_shift, int32_t* nnei, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Neighbour rows of the current positions from candidate rows built earlier

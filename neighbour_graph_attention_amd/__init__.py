@@ -29,6 +29,7 @@ from ._lib import (  # noqa: F401
     load,
     nl_build,
     local_attn_forward,
+    nl_build_batch,
     nl_build_workspace_bytes,
     nl_max_displacement,
     nl_refine,

@@ -26,7 +26,8 @@ EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "
            "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward",
            "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward",
            "nga_step_graph_create", "nga_step_graph_launch", "nga_step_graph_destroy",
-           "nl_refine", "nl_max_displacement")
+           "nl_refine", "nl_max_displacement", "nl_build_batch_workspace_bytes",
+           "nl_build_batch")
 
 
 class NGAError(RuntimeError):
@@ -64,6 +65,10 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward_smooth.restype = ctypes.c_int
     lib.block_attn_forward_smooth.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32,
                                               vp, vp, vp, vp, vp, sz, vp]
+    lib.nl_build_batch_workspace_bytes.restype = sz
+    lib.nl_build_batch_workspace_bytes.argtypes = [i32, vp, vp, dbl]
+    lib.nl_build_batch.restype = ctypes.c_int
+    lib.nl_build_batch.argtypes = [vp, i32, vp, vp, dbl, i32, vp, vp, vp, vp, sz, vp]
     lib.nl_refine.restype = ctypes.c_int
     lib.nl_refine.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.nl_max_displacement.restype = ctypes.c_int
@@ -495,3 +500,32 @@ def nl_max_displacement(pos: torch.Tensor, pos_ref: torch.Tensor, box,
     _check(lib.nl_max_displacement(_ptr(pos), _ptr(pos_ref), n, _box3(box), _ptr(out),
                                    _stream(dev)), "nl_max_displacement")
     return out
+
+
+def nl_build_batch(pos: torch.Tensor, atom_ptr, boxes, rcut: float, sel: int, *, nbr=None,
+                   nbr_shift=None, nnei=None, ws: Workspace | None = None):
+    """Neighbour rows of several structures: pos [N][3] concatenated, atom_ptr [B+1] (host
+    sequence), boxes [B][3] (host).  Returns (nbr [N][sel], nbr_shift [N][sel][3], nnei [N])
+    with indices into the concatenated arrays."""
+    lib = load()
+    dev = pos.device
+    ap = (ctypes.c_int64 * len(atom_ptr))(*[int(v) for v in atom_ptr])
+    flat = [float(v) for b in boxes for v in b]
+    bx = (ctypes.c_double * len(flat))(*flat)
+    nstruct = len(atom_ptr) - 1
+    if len(flat) != 3 * nstruct:
+        raise ValueError("boxes must be [len(atom_ptr) - 1][3]")
+    n = int(atom_ptr[-1])
+    _need(pos, "pos", torch.float64, (n, 3), dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    nbr = torch.empty((n, sel), **i32) if nbr is None else nbr
+    nbr_shift = torch.empty((n, sel, 3), **i32) if nbr_shift is None else nbr_shift
+    nnei = torch.empty((n,), **i32) if nnei is None else nnei
+    need = int(lib.nl_build_batch_workspace_bytes(nstruct, ap, bx, float(rcut)))
+    if need == 0:
+        raise NGAError(NGA_EINVAL, "nl_build_batch")
+    ws = _ws(ws, dev, need)
+    rc = lib.nl_build_batch(_ptr(pos), nstruct, ap, bx, float(rcut), int(sel), _ptr(nbr),
+                            _ptr(nbr_shift), _ptr(nnei), ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "nl_build_batch")
+    return nbr, nbr_shift, nnei

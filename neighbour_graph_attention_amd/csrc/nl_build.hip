@@ -26,6 +26,9 @@
 
 #include "nga_internal.h"
 
+#include <algorithm>
+#include <vector>
+
 namespace nga {
 
 namespace {
@@ -137,6 +140,49 @@ bin_kernel(const double* __restrict__ pos, int n, Geom g, int32_t* __restrict__ 
     atom_slot[i] = atomicAdd(&cell_count[cell], 1);
 }
 
+// A structure of a batch: its geometry, first global cell and first atom.
+struct BatchGeom {
+    Geom g;
+    int64_t cell_base;
+    int64_t atom_base;
+};
+
+// Last b in [0, nb) with ptr[b] <= v (ptr[0] = 0 <= v, ptr non-decreasing).
+__device__ inline int find_segment(const int64_t* ptr, int nb, int64_t v) {
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ptr[mid] <= v) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// bin_kernel for a batch: atom i belongs to the structure whose atom range holds it, and its
+// cell index is that structure's first cell plus its cell within the structure's box.
+__global__ void __launch_bounds__(256)
+bin_batch_kernel(const double* __restrict__ pos, int n, const BatchGeom* __restrict__ table,
+                 const int64_t* __restrict__ atom_ptr, int n_structs,
+                 int32_t* __restrict__ cell_count, int32_t* __restrict__ atom_cell,
+                 int32_t* __restrict__ atom_slot, uint32_t* status) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int b = find_segment(atom_ptr, n_structs, i);
+    const Geom& g = table[b].g;
+    int c[3];
+    bool bad = false;
+    for (int a = 0; a < 3; ++a) {
+        double x = pos[3 * (int64_t)i + a];
+        bool ok = (x >= 0.0) && (x < g.L[a]);
+        bad |= !ok;
+        int ci = ok ? (int)(x * g.inv_h[a]) : 0;
+        c[a] = ci < g.nc[a] ? ci : g.nc[a] - 1;
+    }
+    if (bad) raise_bits(status, kBitBox);
+    int cell = (int)table[b].cell_base + (c[2] * g.nc[1] + c[1]) * g.nc[0] + c[0];
+    atom_cell[i] = cell;
+    atom_slot[i] = atomicAdd(&cell_count[cell], 1);
+}
+
 __global__ void __launch_bounds__(256)
 scatter_kernel(const double* __restrict__ pos, int n, const int64_t* __restrict__ cell_start,
                const int32_t* __restrict__ atom_cell, const int32_t* __restrict__ atom_slot,
@@ -162,6 +208,9 @@ __device__ inline int shift_z(int code) { return (code & 255) - 128; }
 
 struct SelectArgs {
     Geom g;
+    const BatchGeom* table;   // batch: per-structure geometry (g unused)
+    const int64_t* cell_ptr;  // batch: first global cell per structure, [n_structs + 1]
+    int n_structs;
     double rc2;
     int n;
     int sel;
@@ -337,31 +386,43 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, int32_
 // time and walks the stencil cells, reading their cell-sorted positions with coalesced
 // loads, testing the pinned fp64 distance and compacting the accepted candidates into its
 // LDS list with ballot / mbcnt.
+// BATCH: the cells of several structures, each block finding its structure's geometry.
+template <bool BATCH>
 __global__ void __launch_bounds__(kNlBlock)
 select_kernel(SelectArgs A) {
+    const int gcell = blockIdx.x;
+    const int c0 = (int)A.cell_start[gcell];
+    const int c1 = (int)A.cell_start[gcell + 1];
+    if (c0 == c1 || (int)blockIdx.y * kNlWaves >= c1 - c0) return;  // uniform per block
+    Geom g;
+    int cbase = 0;
+    if constexpr (BATCH) {
+        const int b = find_segment(A.cell_ptr, A.n_structs, gcell);
+        g = A.table[b].g;
+        cbase = (int)A.cell_ptr[b];
+    } else {
+        g = A.g;
+    }
+
     extern __shared__ __align__(16) unsigned char nl_smem[];
     WaveList* lists = reinterpret_cast<WaveList*>(nl_smem);
     int* s_start = reinterpret_cast<int*>(nl_smem + kNlWaves * sizeof(WaveList));
-    int* s_len = s_start + A.g.stencil;
-    int* s_code = s_len + A.g.stencil;
+    int* s_len = s_start + g.stencil;
+    int* s_code = s_len + g.stencil;
 
-    const int ncx = A.g.nc[0], ncy = A.g.nc[1], ncz = A.g.nc[2];
-    const int cell = blockIdx.x;
-    const int c0 = (int)A.cell_start[cell];
-    const int c1 = (int)A.cell_start[cell + 1];
-    if (c0 == c1 || (int)blockIdx.y * kNlWaves >= c1 - c0) return;  // uniform per block
-
+    const int ncx = g.nc[0], ncy = g.nc[1], ncz = g.nc[2];
+    const int cell = gcell - cbase;
     Stencil st;
     st.cx = cell % ncx;
     st.cy = (cell / ncx) % ncy;
     st.cz = cell / (ncx * ncy);
-    const int S = A.g.stencil;
+    const int S = g.stencil;
     for (int e = threadIdx.x; e < S; e += kNlBlock) {
         int w, code;
-        stencil_entry(ncx, ncy, ncz, A.g.reach[0], A.g.reach[1], A.g.reach[2], st, e, &w, &code);
-        const int64_t b = A.cell_start[w];
+        stencil_entry(ncx, ncy, ncz, g.reach[0], g.reach[1], g.reach[2], st, e, &w, &code);
+        const int64_t b = A.cell_start[cbase + w];
         s_start[e] = (int)b;
-        s_len[e] = (int)(A.cell_start[w + 1] - b);
+        s_len[e] = (int)(A.cell_start[cbase + w + 1] - b);
         s_code[e] = code;
     }
     __syncthreads();
@@ -392,7 +453,7 @@ select_kernel(SelectArgs A) {
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     WaveList& L = lists[wave];
     const int zero_code = (128 << 16) | (128 << 8) | 128;
-    const double Lx = A.g.L[0], Ly = A.g.L[1], Lz = A.g.L[2];
+    const double Lx = g.L[0], Ly = g.L[1], Lz = g.L[2];
     const double rc2 = A.rc2;
     const int sel = A.sel;
     const double* __restrict__ sx = A.sx;
@@ -496,8 +557,127 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     A.sx = w.sx; A.sy = w.sy; A.sz = w.sz; A.sidx = w.sidx;
     A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
     A.status = status;
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)g.ncells, (unsigned)A.nsplit), dim3(kNlBlock),
-                       (unsigned)select_lds_bytes(g), s, A);
+    A.table = nullptr;
+    A.cell_ptr = nullptr;
+    A.n_structs = 1;
+    hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)g.ncells, (unsigned)A.nsplit),
+                       dim3(kNlBlock), (unsigned)select_lds_bytes(g), s, A);
+    return last_launch_status();
+}
+
+// ---------------------------------------------------------------------------------------
+// Batches of structures: one launch sequence for many boxes.  The cells of all structures are
+// numbered one after the other, so counting, scanning and scattering run unchanged over the
+// whole batch; binning and selection look up each atom's / cell's structure.
+
+struct BatchPlan {
+    std::vector<BatchGeom> table;
+    std::vector<int64_t> atom_ptr;  // [n_structs + 1]
+    std::vector<int64_t> cell_ptr;  // [n_structs + 1]
+    int64_t n_atoms = 0;
+    int64_t n_cells = 0;
+    int max_stencil = 1;
+    int nsplit = 1;
+};
+
+bool plan_batch(int32_t n_structs, const int64_t* atom_ptr, const double* boxes, double rcut,
+                BatchPlan* p) {
+    if (n_structs < 1 || !atom_ptr || !boxes || atom_ptr[0] != 0) return false;
+    p->table.resize(n_structs);
+    p->atom_ptr.assign(atom_ptr, atom_ptr + n_structs + 1);
+    p->cell_ptr.resize((size_t)n_structs + 1);
+    p->cell_ptr[0] = 0;
+    double max_per_cell = 0.0;
+    for (int32_t b = 0; b < n_structs; ++b) {
+        const int64_t nb = atom_ptr[b + 1] - atom_ptr[b];
+        if (nb < 0) return false;
+        Geom g;
+        if (!make_geom(nb, boxes + 3 * (size_t)b, rcut, &g)) return false;
+        p->table[b].g = g;
+        p->table[b].cell_base = p->cell_ptr[b];
+        p->table[b].atom_base = atom_ptr[b];
+        p->cell_ptr[b + 1] = p->cell_ptr[b] + g.ncells;
+        p->max_stencil = std::max(p->max_stencil, g.stencil);
+        max_per_cell = std::max(max_per_cell, (double)nb / (double)g.ncells);
+    }
+    p->n_atoms = atom_ptr[n_structs];
+    p->n_cells = p->cell_ptr[n_structs];
+    if (p->n_atoms >= INT32_MAX || p->n_cells >= INT32_MAX) return false;
+    p->nsplit = std::max(1, std::min((int)std::ceil(max_per_cell / (2.0 * kNlWaves)), 4096));
+    return true;
+}
+
+struct BatchWs {
+    WsLayout w;
+    BatchGeom* table;
+    int64_t* atom_ptr;
+    int64_t* cell_ptr;
+    size_t bytes;
+};
+
+BatchWs carve_batch(void* ws, const BatchPlan& p) {
+    Geom all;
+    all.ncells = p.n_cells;
+    BatchWs b;
+    b.w = carve(ws, p.n_atoms, all);
+    Carver cv(ws);
+    cv.off = b.w.bytes;
+    b.table = cv.take<BatchGeom>(p.table.size());
+    b.atom_ptr = cv.take<int64_t>(p.atom_ptr.size());
+    b.cell_ptr = cv.take<int64_t>(p.cell_ptr.size());
+    b.bytes = cv.off;
+    return b;
+}
+
+int launch_nl_batch(const double* pos, const BatchPlan& p, double rcut, int32_t sel,
+                    int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, hipStream_t s) {
+    BatchWs b = carve_batch(ws, p);
+    const WsLayout& w = b.w;
+    uint32_t* status = &static_cast<WsHeader*>(ws)->status;
+    // The structure table is host data: upload it, and wait, so that nothing here outlives
+    // the call.
+    int rc = hip_status(hipMemcpyAsync(b.table, p.table.data(), p.table.size() * sizeof(BatchGeom),
+                                       hipMemcpyHostToDevice, s));
+    if (!rc) rc = hip_status(hipMemcpyAsync(b.atom_ptr, p.atom_ptr.data(),
+                                            p.atom_ptr.size() * sizeof(int64_t),
+                                            hipMemcpyHostToDevice, s));
+    if (!rc) rc = hip_status(hipMemcpyAsync(b.cell_ptr, p.cell_ptr.data(),
+                                            p.cell_ptr.size() * sizeof(int64_t),
+                                            hipMemcpyHostToDevice, s));
+    if (!rc) rc = hip_status(hipStreamSynchronize(s));
+    if (rc) return rc;
+    const int ni = (int)p.n_atoms;
+    const int ns = (int)p.table.size();
+    hipLaunchKernelGGL(clear_i32_kernel, dim3((unsigned)((p.n_cells + 255) / 256)), dim3(256), 0,
+                       s, w.cell_count, p.n_cells);
+    if (ni > 0)
+        hipLaunchKernelGGL(bin_batch_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,
+                           b.table, b.atom_ptr, ns, w.cell_count, w.atom_cell, w.atom_slot,
+                           status);
+    if ((rc = last_launch_status())) return rc;
+    if ((rc = scan_counts_tile_sums(w.cell_count, p.n_cells, w.tile_sums, s))) return rc;
+    if ((rc = scan_counts_finish(w.cell_count, p.n_cells, w.tile_sums, w.cell_start, s)))
+        return rc;
+    if (ni == 0) return NGA_OK;
+    hipLaunchKernelGGL(scatter_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,
+                       w.cell_start, w.atom_cell, w.atom_slot, w.sx, w.sy, w.sz, w.sidx);
+    if ((rc = last_launch_status())) return rc;
+    SelectArgs A;
+    A.g = p.table[0].g;
+    A.table = b.table;
+    A.cell_ptr = b.cell_ptr;
+    A.n_structs = ns;
+    A.rc2 = rcut * rcut;
+    A.n = ni;
+    A.sel = sel;
+    A.nsplit = p.nsplit;
+    A.cell_start = w.cell_start;
+    A.sx = w.sx; A.sy = w.sy; A.sz = w.sz; A.sidx = w.sidx;
+    A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
+    A.status = status;
+    const size_t lds = kNlWaves * sizeof(WaveList) + 3 * sizeof(int) * (size_t)p.max_stencil;
+    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)p.n_cells, (unsigned)A.nsplit),
+                       dim3(kNlBlock), (unsigned)lds, s, A);
     return last_launch_status();
 }
 
@@ -615,6 +795,28 @@ max_displacement_kernel(const double* __restrict__ pos, const double* __restrict
 }  // namespace
 
 }  // namespace nga
+
+extern "C" size_t nl_build_batch_workspace_bytes(int32_t n_structs, const int64_t* h_atom_ptr,
+                                                 const double* h_boxes, double rcut) {
+    nga::BatchPlan p;
+    if (!nga::plan_batch(n_structs, h_atom_ptr, h_boxes, rcut, &p)) return 0;
+    return nga::carve_batch(nullptr, p).bytes;
+}
+
+extern "C" int nl_build_batch(const double* pos, int32_t n_structs, const int64_t* h_atom_ptr,
+                              const double* h_boxes, double rcut, int32_t sel, int32_t* nbr,
+                              int32_t* nbr_shift, int32_t* nnei, void* ws, size_t ws_bytes,
+                              void* stream) {
+    using namespace nga;
+    BatchPlan p;
+    if (!plan_batch(n_structs, h_atom_ptr, h_boxes, rcut, &p)) return NGA_EINVAL;
+    if (sel < 1) return NGA_EINVAL;
+    if (p.n_atoms > 0 && (!pos || !nbr || !nbr_shift || !nnei)) return NGA_EINVAL;
+    if (!ws || ws_bytes < carve_batch(nullptr, p).bytes) return NGA_EWORKSPACE;
+    if (p.n_atoms == 0) return NGA_OK;
+    return launch_nl_batch(pos, p, rcut, sel, nbr, nbr_shift, nnei, ws,
+                           static_cast<hipStream_t>(stream));
+}
 
 extern "C" int nl_refine(const double* pos, int64_t n_atoms, const double* h_box, double rcut,
                          int32_t sel, const int32_t* cand_nbr, const int32_t* cand_shift,

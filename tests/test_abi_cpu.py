@@ -204,6 +204,31 @@ def test_nl_refine_and_displacement_reject_bad_arguments():
     assert lib.nl_max_displacement(None, FAKE, 10, box, FAKE, None) == L.NGA_EINVAL
 
 
+def test_nl_build_batch_rejects_bad_structures():
+    lib = nga.load()
+    ap = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    bx = lambda *v: (ctypes.c_double * len(v))(*v)
+    boxes = bx(5.0, 5.0, 5.0, 6.0, 6.0, 6.0)
+    assert lib.nl_build_batch_workspace_bytes(2, ap(0, 10, 25), boxes, 2.0) > 0
+    assert lib.nl_build_batch_workspace_bytes(0, ap(0), boxes, 2.0) == 0         # no structure
+    assert lib.nl_build_batch_workspace_bytes(2, ap(1, 10, 25), boxes, 2.0) == 0  # not from 0
+    assert lib.nl_build_batch_workspace_bytes(2, ap(0, 10, 5), boxes, 2.0) == 0   # decreasing
+    assert lib.nl_build_batch_workspace_bytes(2, ap(0, 10, 25), bx(5.0, 5.0, 5.0, 6.0, -1.0, 6.0),
+                                              2.0) == 0                           # bad box
+    assert lib.nl_build_batch_workspace_bytes(2, ap(0, 10, 25), boxes, 0.0) == 0  # rcut
+
+    def call(sel=8, ws=FAKE, wsb=1 << 40, pos=FAKE):
+        return lib.nl_build_batch(pos, 2, ap(0, 10, 25), boxes, 2.0, sel, FAKE, FAKE, FAKE, ws,
+                                  wsb, None)
+
+    assert call(sel=0) == L.NGA_EINVAL
+    assert call(pos=None) == L.NGA_EINVAL
+    assert call(ws=None) == L.NGA_EWORKSPACE
+    assert call(wsb=64) == L.NGA_EWORKSPACE
+    assert lib.nl_build_batch(None, 2, ap(0, 0, 0), boxes, 2.0, 8, None, None, None, FAKE,
+                              1 << 40, None) == L.NGA_OK                          # no atoms
+
+
 def test_attention_workspace_and_variant_queries():
     lib = nga.load()
     assert lib.block_attn_workspace_bytes(9, 10, 8, 8, 2, 1) == 0
