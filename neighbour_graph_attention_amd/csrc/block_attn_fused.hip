@@ -146,6 +146,12 @@ constexpr float kSplitMax = 32768.f;
 
 // LDS block row: 64 hi halves, 64 lo halves, 16 bytes of padding (272 bytes) -- or, between
 // layers, the row's C floats.
+// Slot of 8-byte chunk k (channels 4k .. 4k+3) in the hi and in the lo halves of block row a:
+// rows 8..15 of every 16-row tile swap neighbouring chunks.  An operand read has lane
+// (g, i) take chunk g (plus a multiple of 4) of row i; with the 272-byte row stride rows i and
+// i+8 of a tile would otherwise fall on the same LDS banks.
+__device__ inline int chunk_slot(int k, int a) { return k ^ ((a >> 3) & 1); }
+
 template <int H>
 struct Lds {
     static constexpr int C = 16 * H;
@@ -201,6 +207,9 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
     constexpr int MAT = H * 64 * U;  // h8 per packed matrix
     const int g = lane >> 4;
     const int li = lane & 15;
+    // Byte offset of this lane's channels 4g .. 4g+3 within the hi (and lo) halves of its
+    // block row 16t + li, chunks swizzled as chunk_slot.
+    const int xo = 8 * chunk_slot(g, li);
     const int eq = A.expo[4 * layer + 0], ek = A.expo[4 * layer + 1];
     const int ev = A.expo[4 * layer + 2], eo = A.expo[4 * layer + 3];
     // K and Q leave the projections scaled by 2^(ex + ek) and 2^(ex + eq); values and outputs
@@ -222,8 +231,8 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
         f4 k = {0.f, 0.f, 0.f, 0.f}, v = k;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const h8 xh = dup_read(row + 2 * (16 * u + 4 * g));
-            const h8 xl = dup_read(row + 2 * C + 2 * (16 * u + 4 * g));
+            const h8 xh = dup_read(row + 32 * u + xo);
+            const h8 xl = dup_read(row + 2 * C + 32 * u + xo);
             k = mfma16(wk[u], xh, k);
             k = mfma16(wk[u], xl, k);
             v = mfma16(xh, wv[u], v);
@@ -273,8 +282,8 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
             const unsigned char* row = sX + (16 * qt + li) * RB;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const h8 xh = dup_read(row + 2 * (16 * u + 4 * g));
-                const h8 xl = dup_read(row + 2 * C + 2 * (16 * u + 4 * g));
+                const h8 xh = dup_read(row + 32 * u + xo);
+                const h8 xl = dup_read(row + 2 * C + 32 * u + xo);
                 q = mfma16(wq[u], xh, q);
                 q = mfma16(wq[u], xl, q);
             }
@@ -411,8 +420,9 @@ __device__ inline int split_block(f4 (&vals)[PER], int chunks, unsigned char* sX
             lo[i] = p[1];
         }
         unsigned char* row = sX + a * Lds<H>::RB;
-        *reinterpret_cast<h4*>(row + 2 * (4 * c4)) = hi;
-        *reinterpret_cast<h4*>(row + 2 * C + 2 * (4 * c4)) = lo;
+        const int slot = chunk_slot(c4, a);
+        *reinterpret_cast<h4*>(row + 8 * slot) = hi;
+        *reinterpret_cast<h4*>(row + 2 * C + 8 * slot) = lo;
     }
     return e;
 }
