@@ -258,9 +258,23 @@ __device__ inline uint64_t lo_key(const WaveList& L, int p) {
     return ((uint64_t)(uint32_t)L.j[p] << 24) | (uint64_t)(uint32_t)L.code[p];
 }
 
-// Bitonic sort of 64*NS 64-bit words held NS per lane (element e = lane*NS + q), ascending.
+// Sort words: a 23-bit distance class above the 9-bit list index of the candidate.
+constexpr int kIndexBits = 9;
+static_assert(NGA_ROW_CAP <= (1 << kIndexBits), "list index must fit the sort word");
+constexpr uint32_t kIndexMask = (1u << kIndexBits) - 1;
+constexpr double kClassMax = (double)((1u << (32 - kIndexBits)) - 2);
+
+// Distance class of r2 in [0, rc2): floor(r2 * 2^23 / rc2), capped below the padding word's
+// class.  Non-decreasing in r2, so ordering by class and then re-ranking each run of equal
+// classes by the full key gives the full-key order.
+__device__ inline uint32_t dist_class(uint64_t r2_bits, double qscale) {
+    const double s = __longlong_as_double((long long)r2_bits) * qscale;
+    return s < kClassMax ? (uint32_t)s : (uint32_t)kClassMax;
+}
+
+// Bitonic sort of 64*NS 32-bit words held NS per lane (element e = lane*NS + q), ascending.
 template <int NS>
-__device__ inline void bitonic_sort(uint64_t (&k)[NS], int lane) {
+__device__ inline void bitonic_sort(uint32_t (&k)[NS], int lane) {
     constexpr int M = 64 * NS;
 #pragma unroll
     for (int size = 2; size <= M; size <<= 1) {
@@ -273,20 +287,19 @@ __device__ inline void bitonic_sort(uint64_t (&k)[NS], int lane) {
                     const int o = q | stride;
                     const int e = lane * NS + q;
                     const bool ascending = (e & size) == 0;
-                    if ((k[o] < k[q]) == ascending) {
-                        const uint64_t t = k[q]; k[q] = k[o]; k[o] = t;
-                    }
+                    const uint32_t lo = min(k[q], k[o]), hi = max(k[q], k[o]);
+                    k[q] = ascending ? lo : hi;
+                    k[o] = ascending ? hi : lo;
                 }
             } else {
                 const int lx = stride / NS;
 #pragma unroll
                 for (int q = 0; q < NS; ++q) {
                     const int e = lane * NS + q;
-                    const uint64_t ok = __shfl_xor(k[q], lx, 64);
+                    const uint32_t ok = __shfl_xor(k[q], lx, 64);
                     const bool ascending = (e & size) == 0;
                     const bool lower = (e & stride) == 0;
-                    const bool take = lower == ascending ? ok < k[q] : k[q] < ok;
-                    if (take) k[q] = ok;
+                    k[q] = lower == ascending ? min(ok, k[q]) : max(ok, k[q]);
                 }
             }
         }
@@ -306,50 +319,51 @@ __device__ inline bool full_less(const WaveList& L, int a, int b) {
 }
 
 // Sort the wave's `count` candidates by (r2, j, shift) and write the first `keep` as row i.
-// The bitonic network sorts one 64-bit word per candidate: the upper 32 bits of the r2 bit
-// pattern above the list index.  Entries whose upper 32 bits equal a neighbour's are then
-// re-ranked inside their run by the full key (rare: it takes r2 values equal to about 1e-6
-// relative, such as the exact ties of ideal lattices).
+// The bitonic network sorts one 32-bit word per candidate: its distance class (dist_class,
+// qscale = 2^23 / rc2) above its list index.  Entries whose class equals a neighbour's are
+// then re-ranked inside their run by the full key (runs are rare: classes are rc2 * 2^-23
+// wide, so it takes r2 values within about 1e-5 A^2 of each other at rcut = 8 A, such as the
+// exact ties of ideal lattices).
 template <int NS>
-__device__ void sort_and_write(WaveList& L, int count, int keep, int sel, int32_t* row,
-                               int32_t* rsh, int lane) {
-    uint64_t k[NS];
+__device__ void sort_and_write(WaveList& L, int count, int keep, int sel, double qscale,
+                               int32_t* row, int32_t* rsh, int lane) {
+    uint32_t k[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         const int e = lane * NS + q;
-        k[q] = e < count ? ((L.r2[e] >> 32) << 32) | (uint64_t)e : ~0ull;
+        k[q] = e < count ? (dist_class(L.r2[e], qscale) << kIndexBits) | (uint32_t)e : ~0u;
     }
     bitonic_sort<NS>(k, lane);
 
-    const uint64_t prev_last = __shfl_up(k[NS - 1], 1, 64);
+    const uint32_t prev_last = __shfl_up(k[NS - 1], 1, 64);
     bool tie = false;
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         const int e = lane * NS + q;
-        const uint64_t before = q > 0 ? k[q - 1] : prev_last;
-        if (e > 0 && e < count && (before >> 32) == (k[q] >> 32)) tie = true;
+        const uint32_t before = q > 0 ? k[q - 1] : prev_last;
+        if (e > 0 && e < count && (before >> kIndexBits) == (k[q] >> kIndexBits)) tie = true;
     }
     int pos[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) pos[q] = lane * NS + q;
     if (__ballot(tie)) {
-        // Publish the sorted list indices, then rank each entry of a run of equal upper
-        // words by the full key.
+        // Publish the sorted list indices, then rank each entry of a run of equal classes by
+        // the full key.
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
             const int e = lane * NS + q;
-            if (e < count) L.pay[e] = (int)(uint32_t)k[q];
+            if (e < count) L.pay[e] = (int)(k[q] & kIndexMask);
         }
         wave_sync_lds();
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
             const int e = lane * NS + q;
             if (e >= count) continue;
-            const uint32_t hi = (uint32_t)(k[q] >> 32);
-            const int me = (int)(uint32_t)k[q];
+            const uint32_t cls = k[q] >> kIndexBits;
+            const int me = (int)(k[q] & kIndexMask);
             int rs = e, re = e + 1;
-            while (rs > 0 && (uint32_t)(L.r2[L.pay[rs - 1]] >> 32) == hi) --rs;
-            while (re < count && (uint32_t)(L.r2[L.pay[re]] >> 32) == hi) ++re;
+            while (rs > 0 && dist_class(L.r2[L.pay[rs - 1]], qscale) == cls) --rs;
+            while (re < count && dist_class(L.r2[L.pay[re]], qscale) == cls) ++re;
             if (re - rs == 1) continue;
             int rank = 0;
             for (int t = rs; t < re; ++t) rank += full_less(L, L.pay[t], me);
@@ -363,7 +377,7 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, int32_
         if (e < count) {
             const int at = pos[q];
             if (at < keep) {
-                const int p = (int)(uint32_t)k[q];
+                const int p = (int)(k[q] & kIndexMask);
                 const int code = L.code[p];
                 row[at] = L.j[p];
                 rsh[3 * at + 0] = shift_x(code);
@@ -515,10 +529,11 @@ select_kernel(SelectArgs A) {
         const int keep = count < sel ? count : sel;
         int32_t* row = A.nbr + (int64_t)i * sel;
         int32_t* rsh = A.nbr_shift + (int64_t)i * sel * 3;
-        if (count <= 64) sort_and_write<1>(L, count, keep, sel, row, rsh, lane);
-        else if (count <= 128) sort_and_write<2>(L, count, keep, sel, row, rsh, lane);
-        else if (count <= 256) sort_and_write<4>(L, count, keep, sel, row, rsh, lane);
-        else sort_and_write<8>(L, count, keep, sel, row, rsh, lane);
+        const double qscale = 8388608.0 / rc2;
+        if (count <= 64) sort_and_write<1>(L, count, keep, sel, qscale, row, rsh, lane);
+        else if (count <= 128) sort_and_write<2>(L, count, keep, sel, qscale, row, rsh, lane);
+        else if (count <= 256) sort_and_write<4>(L, count, keep, sel, qscale, row, rsh, lane);
+        else sort_and_write<8>(L, count, keep, sel, qscale, row, rsh, lane);
         if (lane == 0) A.nnei[i] = keep;
         wave_sync_lds();
     }
@@ -757,10 +772,11 @@ __global__ void __launch_bounds__(kNlBlock) refine_kernel(RefineArgs A) {
     const int keep = count < A.sel ? count : A.sel;
     int32_t* row = A.nbr + (int64_t)i * A.sel;
     int32_t* rsh = A.nbr_shift + (int64_t)i * A.sel * 3;
-    if (count <= 64) sort_and_write<1>(L, count, keep, A.sel, row, rsh, lane);
-    else if (count <= 128) sort_and_write<2>(L, count, keep, A.sel, row, rsh, lane);
-    else if (count <= 256) sort_and_write<4>(L, count, keep, A.sel, row, rsh, lane);
-    else sort_and_write<8>(L, count, keep, A.sel, row, rsh, lane);
+    const double qscale = 8388608.0 / A.rc2;
+    if (count <= 64) sort_and_write<1>(L, count, keep, A.sel, qscale, row, rsh, lane);
+    else if (count <= 128) sort_and_write<2>(L, count, keep, A.sel, qscale, row, rsh, lane);
+    else if (count <= 256) sort_and_write<4>(L, count, keep, A.sel, qscale, row, rsh, lane);
+    else sort_and_write<8>(L, count, keep, A.sel, qscale, row, rsh, lane);
     if (lane == 0) A.nnei[i] = keep;
     if (__ballot(bad) && lane == 0) raise_bits(A.status, kBitIndex);
 }

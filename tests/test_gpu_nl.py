@@ -139,6 +139,31 @@ def test_hand_cases(oracle_mod):
     assert g["row_ptr"].tolist() == [0, 0, 0]
 
 
+def test_near_ties_within_one_distance_class(oracle_mod):
+    """Neighbours whose r2 differ by far less than rc2 * 2^-23 (the resolution of the first
+    sort pass) but are not equal, in the opposite order to their indices, plus six exact
+    ties on the axes; sel cuts through the run.  The rows must follow the full key
+    (r2, j, shift) exactly."""
+    rng = np.random.default_rng(41)
+    centre = np.array([5.0, 5.0, 5.0])
+    k = 20
+    dirs = rng.normal(size=(k, 3))
+    dirs /= np.linalg.norm(dirs, axis=1, keepdims=True)
+    radii = 2.0 + 1e-8 * np.arange(k, 0, -1)  # atom 1 farthest, atom k nearest
+    shell = centre + dirs * radii[:, None]
+    axes = centre + 2.0 * np.array([[1, 0, 0], [-1, 0, 0], [0, 1, 0], [0, -1, 0],
+                                    [0, 0, 1], [0, 0, -1]], dtype=np.float64)
+    pos = np.concatenate([centre[None], shell, axes])
+    for sel in (10, 23, 40):
+        g = _gpu_csr(pos, (10.0, 10.0, 10.0), 4.0, sel)
+        _assert_same_csr(g, oracle_mod.nl_full(pos, (10.0, 10.0, 10.0), 4.0, sel))
+    # the first row really is ordered by r2 among the near-tied shell atoms
+    g = _gpu_csr(pos, (10.0, 10.0, 10.0), 4.0, 40)
+    row0 = g["col"][g["row_ptr"][0]:g["row_ptr"][1]]
+    shell_order = [j for j in row0 if 1 <= j <= k]
+    assert shell_order == sorted(shell_order, reverse=True)
+
+
 def test_empty_and_single_atom():
     pos = torch.zeros((0, 3), dtype=torch.float64, device=DEV)
     nbr, nbr_shift, nnei = nga.nl_build(pos, (5.0, 5.0, 5.0), 2.0, 4)
