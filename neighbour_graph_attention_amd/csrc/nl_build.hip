@@ -431,33 +431,72 @@ select_kernel(SelectArgs A) {
     st.cy = (cell / ncx) % ncy;
     st.cz = cell / (ncx * ncy);
     const int S = g.stencil;
-    for (int e = threadIdx.x; e < S; e += kNlBlock) {
-        int w, code;
-        stencil_entry(ncx, ncy, ncz, g.reach[0], g.reach[1], g.reach[2], st, e, &w, &code);
-        const int64_t b = A.cell_start[cbase + w];
-        s_start[e] = (int)b;
-        s_len[e] = (int)(A.cell_start[cbase + w + 1] - b);
-        s_code[e] = code;
-    }
-    __syncthreads();
     // Merge stencil cells that follow each other in memory with the same image shift (the
-    // cells of one x-row away from the box edge) into one segment.
+    // cells of one x-row away from the box edge) into one segment; empty cells drop out.
     __shared__ int s_nseg;
-    if (threadIdx.x == 0) {
-        int nseg = 0;
-        for (int e = 0; e < S; ++e) {
-            const int b = s_start[e], l = s_len[e], code = s_code[e];
-            if (l == 0) continue;
-            if (nseg > 0 && s_code[nseg - 1] == code && s_start[nseg - 1] + s_len[nseg - 1] == b) {
-                s_len[nseg - 1] += l;
-            } else {
-                s_start[nseg] = b;
-                s_len[nseg] = l;
-                s_code[nseg] = code;
-                ++nseg;
+    if (S <= 64) {
+        // One wavefront: entry e in lane e; a non-empty entry starts a segment unless the
+        // previous non-empty entry has its shift and ends where it begins.
+        if (threadIdx.x < 64) {
+            const int e = threadIdx.x;
+            int b = 0, l = 0, code = -1;
+            if (e < S) {
+                int w;
+                stencil_entry(ncx, ncy, ncz, g.reach[0], g.reach[1], g.reach[2], st, e, &w,
+                              &code);
+                const int64_t b64 = A.cell_start[cbase + w];
+                b = (int)b64;
+                l = (int)(A.cell_start[cbase + w + 1] - b64);
             }
+            const bool filled = l > 0;
+            const uint64_t below = e == 0 ? 0ull : (~0ull >> (64 - e));
+            const uint64_t fm = __ballot(filled);
+            const uint64_t fb = fm & below;
+            const int pe = fb ? 63 - __clzll(fb) : e;  // previous non-empty entry
+            const int pb = __shfl(b, pe, 64), pl = __shfl(l, pe, 64), pc = __shfl(code, pe, 64);
+            const bool head = filled && (fb == 0 || pc != code || pb + pl != b);
+            const uint64_t hm = __ballot(head);
+            // The segment headed here ends with the last non-empty entry before the next head.
+            const uint64_t after = e == 63 ? 0ull : (hm & (~0ull << (e + 1)));
+            const int nh = after ? __ffsll((long long)after) - 1 : 64;
+            const uint64_t upto = fm & (nh == 64 ? ~0ull : ((1ull << nh) - 1));
+            const int last = upto ? 63 - __clzll(upto) : e;
+            const int end = __shfl(b + l, last, 64);
+            if (head) {
+                const int sid = __popcll(hm & below);
+                s_start[sid] = b;
+                s_len[sid] = end - b;
+                s_code[sid] = code;
+            }
+            if (e == 0) s_nseg = __popcll(hm);
         }
-        s_nseg = nseg;
+    } else {
+        for (int e = threadIdx.x; e < S; e += kNlBlock) {
+            int w, code;
+            stencil_entry(ncx, ncy, ncz, g.reach[0], g.reach[1], g.reach[2], st, e, &w, &code);
+            const int64_t b = A.cell_start[cbase + w];
+            s_start[e] = (int)b;
+            s_len[e] = (int)(A.cell_start[cbase + w + 1] - b);
+            s_code[e] = code;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int nseg = 0;
+            for (int e = 0; e < S; ++e) {
+                const int b = s_start[e], l = s_len[e], code = s_code[e];
+                if (l == 0) continue;
+                if (nseg > 0 && s_code[nseg - 1] == code &&
+                    s_start[nseg - 1] + s_len[nseg - 1] == b) {
+                    s_len[nseg - 1] += l;
+                } else {
+                    s_start[nseg] = b;
+                    s_len[nseg] = l;
+                    s_code[nseg] = code;
+                    ++nseg;
+                }
+            }
+            s_nseg = nseg;
+        }
     }
     __syncthreads();
     const int nseg = s_nseg;
@@ -539,6 +578,17 @@ select_kernel(SelectArgs A) {
     }
 }
 
+// Work-groups per cell for select: about four centres per wavefront, which amortises each
+// work-group's stencil set-up, unless that leaves fewer than kMinSelectGroups work-groups in
+// all; then more, down to one centre per wavefront.
+constexpr double kMinSelectGroups = 1024.0;
+int select_splits(double per_cell, int64_t ncells) {
+    double ns = std::ceil(per_cell / (4.0 * kNlWaves));
+    if (ns * (double)ncells < kMinSelectGroups)
+        ns = std::min(std::ceil(per_cell / kNlWaves), std::ceil(kMinSelectGroups / (double)ncells));
+    return (int)std::max(1.0, std::min(ns, 4096.0));
+}
+
 size_t select_lds_bytes(const Geom& g) {
     return kNlWaves * sizeof(WaveList) + 3 * sizeof(int) * (size_t)g.stencil;
 }
@@ -565,9 +615,7 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     A.rc2 = rcut * rcut;
     A.n = ni;
     A.sel = sel;
-    double per_cell = (double)n / (double)g.ncells;
-    int nsplit = (int)std::ceil(per_cell / (2.0 * kNlWaves));
-    A.nsplit = std::max(1, std::min(nsplit, 4096));
+    A.nsplit = select_splits((double)n / (double)g.ncells, g.ncells);
     A.cell_start = w.cell_start;
     A.sx = w.sx; A.sy = w.sy; A.sz = w.sz; A.sidx = w.sidx;
     A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
@@ -618,7 +666,7 @@ bool plan_batch(int32_t n_structs, const int64_t* atom_ptr, const double* boxes,
     p->n_atoms = atom_ptr[n_structs];
     p->n_cells = p->cell_ptr[n_structs];
     if (p->n_atoms >= INT32_MAX || p->n_cells >= INT32_MAX) return false;
-    p->nsplit = std::max(1, std::min((int)std::ceil(max_per_cell / (2.0 * kNlWaves)), 4096));
+    p->nsplit = select_splits(max_per_cell, p->n_cells);
     return true;
 }
 
