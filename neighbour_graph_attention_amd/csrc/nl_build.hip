@@ -251,7 +251,7 @@ struct WaveList {
     uint64_t r2[NGA_ROW_CAP];
     int32_t j[NGA_ROW_CAP];
     int32_t code[NGA_ROW_CAP];
-    int32_t pay[NGA_ROW_CAP];
+    uint16_t pay[NGA_ROW_CAP];
 };
 
 __device__ inline uint64_t lo_key(const WaveList& L, int p) {
@@ -352,7 +352,7 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, double
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
             const int e = lane * NS + q;
-            if (e < count) L.pay[e] = (int)(k[q] & kIndexMask);
+            if (e < count) L.pay[e] = (uint16_t)(k[q] & kIndexMask);
         }
         wave_sync_lds();
 #pragma unroll
