@@ -14,7 +14,6 @@ built (``neighbour_graph_attention_amd._build.build()``).
 """
 from ._lib import (  # noqa: F401
     EXPORTS,
-    NGA_ERANGE,
     NGA_F32,
     NGA_F64,
     ROW_CAP,

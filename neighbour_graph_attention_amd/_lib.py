@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnga.so")
 
 NGA_OK, NGA_EINVAL, NGA_EBOX, NGA_EROWCAP, NGA_ECAP, NGA_EDTYPE, NGA_EWORKSPACE, NGA_EHIP, \
-    NGA_EINDEX, NGA_ERANGE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+    NGA_EINDEX = 0, -1, -2, -3, -4, -5, -6, -7, -8
 NGA_F64, NGA_F32 = 0, 1
 ROW_CAP = 512
 

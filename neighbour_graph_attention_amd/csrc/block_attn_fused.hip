@@ -50,6 +50,8 @@
 // hardware reciprocal, and the splits use packed conversions and mixed-precision FMAs.
 #include "block_attn_fused.h"
 
+#include <climits>
+
 namespace nga {
 
 namespace {
@@ -139,10 +141,12 @@ struct FusedArgs {
 };
 
 // Smooth attention rescales each (query, head) output by sum_j e_j / D~, so O is no longer a
-// convex combination of V rows.  Its instances lower the output scale by 2^8, which leaves
-// room for factors up to about 2^9 in the split, and report anything past kSplitMax.
-constexpr int kSmoothHeadroom = 8;
-constexpr float kSplitMax = 32768.f;
+// convex combination of V rows and max |V| no longer bounds it.  Its instances give every
+// query row its own power-of-two scale instead, common to the row's heads: each head's O row
+// is formed as (fraction in [1, 2) of the factor) * O, its magnitude ilogb(max |O|) plus the
+// factor's power of two goes through LDS, and the largest over the heads fixes the shift that
+// brings that row to [2^13, 2^14) before the split.  Y is shifted back by the same power.
+constexpr int kNoMagnitude = INT_MIN / 2;
 
 // LDS block row: 64 hi halves, 64 lo halves, 16 bytes of padding (272 bytes) -- or, between
 // layers, the row's C floats.
@@ -200,7 +204,8 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
                                              unsigned char* __restrict__ sX,
                                              h8 (*__restrict__ sO)[H][64],
                                              h8 (*__restrict__ sWoh)[64], float* red,
-                                             const int lane, const int h) {
+                                             int (*__restrict__ sMag)[16], const int lane,
+                                             const int h) {
     constexpr int C = 16 * H;
     constexpr int U = C / 16;
     constexpr int RB = Lds<H>::RB;
@@ -268,7 +273,7 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
     vmax = red[0];
 #pragma unroll
     for (int w = 1; w < H; ++w) vmax = fmaxf(vmax, red[w]);
-    const int e_o = scale_exponent(vmax) - (SMOOTH ? kSmoothHeadroom : 0);
+    const int e_o = scale_exponent(vmax);
     const float yscale = ldexpf(1.f, -(ex + ev + e_o + eo));
     // V at that scale, split: lane (i, g) of key tile t holds [V_hi, V_lo] of keys
     // 16t + 4g .. 16t + 4g + 3, channel i -- the A operand of O^T = V^T P^T.
@@ -336,19 +341,38 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
             osum = mfma16(va[t], swap_halves(pa), osum);
         }
         f4 o;
+        int e_row = 0;  // smooth: the query row's shift, common to its heads
         if constexpr (SMOOTH) {
-            // sum_j e_j / D~ times the softmax = exp(s_j - ln D~): in place of 1/Z,
-            // exp2(m c1 - 13 - log2(e) ln D~) (P carries 2^13 and the row max).
+            // sum_j e_j / D~ times the softmax = exp(s_j - ln D~): in place of 1/Z the factor
+            // 2^t, t = m c1 - 13 - log2(e) ln D~ (P carries 2^13 and the row max), taken as
+            // 2^k * 2^(t - k) with k = floor(t).
             const int aq = 16 * qt + li;
-            float f = 0.f;
+            float frac = 0.f;
+            int k = 0;
             if (aq < n) {
                 const int64_t row = A.order ? (int64_t)A.order[r0 + aq] : r0 + aq;
-                if (row >= 0 && row < A.n_edges)
-                    f = exp2f(mc - kLog2e * A.ldt[((int64_t)layer * A.n_edges + row) * H + h]);
+                if (row >= 0 && row < A.n_edges) {
+                    const float t = mc - kLog2e * A.ldt[((int64_t)layer * A.n_edges + row) * H + h];
+                    const float kf = floorf(fminf(fmaxf(t, -4096.f), 4096.f));
+                    frac = exp2f(t - kf);
+                    k = (int)kf;
+                }
             }
-            o = osum * f;
-            const float om = fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3])));
-            if (!(om <= kSplitMax)) raise_bits(A.status, kBitRange);
+            o = osum * frac;
+            float om = fmaxf(fmaxf(fabsf(o[0]), fabsf(o[1])), fmaxf(fabsf(o[2]), fabsf(o[3])));
+            om = fmaxf(om, __shfl_xor(om, 16, 64));
+            om = fmaxf(om, __shfl_xor(om, 32, 64));
+            // A zero row has no magnitude; a non-finite one keeps its scale (the infinity or
+            // NaN reaches y as in fp32 arithmetic).
+            const int mag = om > 0.f && om <= 3.402823466e38f ? ilogbf(om) + k : kNoMagnitude;
+            if (g == 0) sMag[h][li] = mag;
+            __syncthreads();
+            int top = sMag[0][li];
+#pragma unroll
+            for (int w = 1; w < H; ++w) top = max(top, sMag[w][li]);
+            e_row = top == kNoMagnitude ? 0 : 13 - top;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = ldexpf(o[r], k + e_row);
         } else {
             o = osum * __builtin_amdgcn_rcpf(z);
         }
@@ -373,7 +397,13 @@ __device__ __forceinline__ void centre_layer(const FusedArgs& A, const h8* __res
             yv = mfma16(wo, oh, yv);
             yv = mfma16(wo, ol, yv);
         }
-        yv *= yscale;
+        if constexpr (SMOOTH) {
+            const int back = -(ex + ev + e_o + eo) - e_row;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yv[r] = ldexpf(yv[r], back);
+        } else {
+            yv *= yscale;
+        }
         const int a = 16 * qt + li;
         if (last) {
             if (a < n) {
@@ -438,6 +468,7 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
     __shared__ h8 sO[2][H][64];
     __shared__ h8 sWo[H][U][64];
     __shared__ float red[H];
+    __shared__ int sMag[H][16];
 
     const int lane = threadIdx.x & 63;
     const int h = threadIdx.x >> 6;
@@ -482,8 +513,8 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
 #define NGA_CASE(T)                                                                            \
     case T:                                                                                    \
         if constexpr (T <= TMAX)                                                               \
-            centre_layer<H, T, SMOOTH>(A, P, layer, ex, r0, n, last, sX, sO, sWo[h], red, lane,  \
-                                       h);                                                     \
+            centre_layer<H, T, SMOOTH>(A, P, layer, ex, r0, n, last, sX, sO, sWo[h], red, sMag, \
+                                       lane, h);                                               \
         break;
             switch (nt) {
                 NGA_CASE(1) NGA_CASE(2) NGA_CASE(3) NGA_CASE(4) NGA_CASE(5) NGA_CASE(6)

@@ -130,7 +130,6 @@ int status_from_bits(uint32_t bits) {
     if (bits & kBitRowCap) return NGA_EROWCAP;
     if (bits & kBitCap) return NGA_ECAP;
     if (bits & kBitIndex) return NGA_EINDEX;
-    if (bits & kBitRange) return NGA_ERANGE;
     return NGA_OK;
 }
 

@@ -17,7 +17,6 @@ enum : uint32_t {
     kBitRowCap = 1u << 1,
     kBitCap = 1u << 2,
     kBitIndex = 1u << 3,
-    kBitRange = 1u << 4,
 };
 
 // Every workspace starts with this header.

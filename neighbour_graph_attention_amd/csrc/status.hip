@@ -17,7 +17,6 @@ extern "C" const char* nga_strerror(int status) {
         case NGA_EWORKSPACE: return "workspace missing or too small";
         case NGA_EHIP: return "HIP runtime error";
         case NGA_EINDEX: return "an index in device data is out of range";
-        case NGA_ERANGE: return "a smooth-attention rescale is beyond the kernel's range";
         default: return "unknown status";
     }
 }

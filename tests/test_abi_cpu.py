@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -10, -1):
+    for code in range(0, -9, -1):
         assert nga.strerror(code) != "unknown status"
     assert nga.strerror(-99) == "unknown status"
 
