@@ -236,6 +236,8 @@ extern "C" size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t
         cv.take<float>(nga::fused_workspace_floats(c, n_layers));
         return cv.off;
     }
+    if (dtype == NGA_F64 && nga::fused_f64_supported(nnei_cap, c, n_heads))
+        return nga::Carver(nullptr).off;  // the status word only
     const size_t es = dtype == NGA_F64 ? sizeof(double) : sizeof(float);
     return nga::carve_generic(nullptr, n_edges, c, n_layers, es).bytes;
 }
@@ -243,6 +245,7 @@ extern "C" size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t
 extern "C" const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads) {
     if (dtype != NGA_F64 && dtype != NGA_F32) return "unsupported";
     if (nga::use_fused(dtype, nnei_cap, c, n_heads)) return nga::fused_name(dtype, c, n_heads);
+    if (dtype == NGA_F64 && nga::fused_f64_supported(nnei_cap, c, n_heads)) return "fused_f64";
     if (dtype == NGA_F64 && nga::f64_mfma_supported(nnei_cap, c, n_heads)) return "mfma_f64";
     return dtype == NGA_F64 ? "generic_f64" : "generic_f32";
 }
@@ -279,6 +282,10 @@ int attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order, int64_
         return run_fused(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
                          weights, x, ldt, y, packed, status, s);
     }
+    if (dtype == NGA_F64 && fused_f64_supported(nnei_cap, c, n_heads))  // checks row_ptr itself
+        return run_fused_f64(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
+                             static_cast<const double*>(weights), static_cast<const double*>(x),
+                             static_cast<const double*>(ldt), static_cast<double*>(y), status, s);
     hipLaunchKernelGGL(check_rows_kernel, dim3(1), dim3(1), 0, s, row_ptr, (int)n_centres, n_edges,
                        status);
     int rc = last_launch_status();

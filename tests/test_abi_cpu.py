@@ -232,12 +232,17 @@ def test_nl_build_batch_rejects_bad_structures():
 def test_attention_workspace_and_variant_queries():
     lib = nga.load()
     assert lib.block_attn_workspace_bytes(9, 10, 8, 8, 2, 1) == 0
-    g = lib.block_attn_workspace_bytes(L.NGA_F64, 1000, 40, 32, 4, 6)
-    assert g >= 1000 * 32 * 8 * 5
-    assert nga.attn_variant(L.NGA_F64, 40, 32, 4) == "mfma_f64"        # head width 8
+    g = lib.block_attn_workspace_bytes(L.NGA_F64, 1000, 90, 64, 4, 6)
+    assert g >= 1000 * 64 * 8 * 5                                       # buffers between launches
+    assert lib.block_attn_workspace_bytes(L.NGA_F64, 1000, 40, 32, 4, 6) <= 256  # fused: status
+    assert nga.attn_variant(L.NGA_F64, 40, 32, 4) == "fused_f64"       # heads of 8, c <= 32
+    assert nga.attn_variant(L.NGA_F64, 64, 32, 2) == "fused_f64"       # heads of 16, rows <= 64
+    assert nga.attn_variant(L.NGA_F64, 40, 24, 3) == "fused_f64"       # three heads of 8
+    assert nga.attn_variant(L.NGA_F64, 65, 32, 4) == "mfma_f64"        # rows past 64
+    assert nga.attn_variant(L.NGA_F64, 40, 64, 4) == "mfma_f64"        # c past 32
     assert nga.attn_variant(L.NGA_F64, 128, 128, 4) == "mfma_f64"      # head width 32, cap 128
     assert nga.attn_variant(L.NGA_F64, 129, 128, 4) == "generic_f64"   # rows past 128
-    assert nga.attn_variant(L.NGA_F64, 40, 24, 3) == "mfma_f64"        # three heads of 8
+    assert nga.attn_variant(L.NGA_F64, 40, 16, 4) == "generic_f64"     # head width 4
     assert nga.attn_variant(L.NGA_F64, 40, 20, 2) == "generic_f64"     # head width 10
     assert nga.attn_variant(L.NGA_F32, 181, 64, 4) == "fused_f32_d16"
     assert nga.attn_variant(L.NGA_F32, 192, 16, 1) == "fused_f32_d16"

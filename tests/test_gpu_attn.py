@@ -100,6 +100,11 @@ CASES = [
     (np.float32, 20, 400, 64, 4, 2, 15),     # rows past 192: generic online-softmax path
     (np.float32, 10, 512, 16, 1, 1, 16),     # rows at the 512-neighbour cap
     (np.float64, 15, 300, 32, 4, 1, 17),     # fp64 rows past 128: generic path
+    (np.float64, 40, 64, 32, 4, 6, 18),      # fused fp64: rows up to its 64 cap, six layers
+    (np.float64, 30, 64, 32, 2, 2, 19),      # fused fp64, heads of 16
+    (np.float64, 30, 50, 16, 1, 3, 20),      # fused fp64, one head of 16
+    (np.float64, 20, 64, 8, 1, 2, 21),       # fused fp64, one head of 8
+    (np.float64, 20, 65, 32, 4, 2, 22),      # rows past 64: fp64 matrix-core path
 ]
 
 
@@ -188,7 +193,8 @@ def test_f32_weight_magnitudes(oracle_mod):
     assert err < TOL[np.float32]
 
 
-@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float64, 32, 4, 60), (np.float32, 64, 4, 181)])
+@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float64, 32, 4, 60), (np.float64, 64, 4, 100),
+                                             (np.float32, 64, 4, 181)])
 def test_order_gather_scatter(oracle_mod, dtype, c, heads, cap):
     rp = W.random_rows(30, cap, 77, min_len=1)
     e = int(rp[-1])
@@ -219,14 +225,24 @@ def test_deterministic_and_cap_independent(dtype, c, heads, cap):
     assert np.array_equal(a, c2)
 
 
-PATH_CASES = [(np.float64, 4), (np.float64, 2), (np.float32, 1)]  # generic, mfma_f64, fused
+PATH_CASES = [  # (dtype, c, heads, kernel path)
+    (np.float64, 16, 4, "generic_f64"),
+    (np.float64, 16, 2, "fused_f64"),
+    (np.float64, 64, 4, "mfma_f64"),
+    (np.float32, 16, 1, "fused_f32_d16"),
+]
 
 
-@pytest.mark.parametrize("dtype,heads", PATH_CASES)
-def test_rows_untouched_outside_centres(dtype, heads):
+def _path_check(dtype, c, heads, cap, variant):
+    assert nga.attn_variant(0 if dtype == np.float64 else 1, cap, c, heads) == variant
+
+
+@pytest.mark.parametrize("dtype,c,heads,variant", PATH_CASES)
+def test_rows_untouched_outside_centres(dtype, c, heads, variant):
+    _path_check(dtype, c, heads, 8, variant)
     rp = np.array([0, 3, 3, 7], np.int64)
-    x = W.make_features(10, 16, 1, dtype)
-    wt = W.make_weights(1, 16, 2, dtype)
+    x = W.make_features(10, c, 1, dtype)
+    wt = W.make_weights(1, c, 2, dtype)
     xt = torch.from_numpy(x).to(DEV)
     y = torch.full_like(xt, 7.0)
     ws = nga.Workspace(DEV)
@@ -236,22 +252,24 @@ def test_rows_untouched_outside_centres(dtype, heads):
     assert torch.all(y[7:] == 7.0)
 
 
-@pytest.mark.parametrize("dtype,heads", PATH_CASES)
-def test_row_over_cap_is_reported(dtype, heads):
+@pytest.mark.parametrize("dtype,c,heads,variant", PATH_CASES)
+def test_row_over_cap_is_reported(dtype, c, heads, variant):
+    _path_check(dtype, c, heads, 10, variant)
     rp = np.array([0, 5, 30], np.int64)
-    x = W.make_features(30, 16, 1, dtype)
-    wt = W.make_weights(1, 16, 2, dtype)
+    x = W.make_features(30, c, 1, dtype)
+    wt = W.make_weights(1, c, 2, dtype)
     ws = nga.Workspace(DEV)
     nga.block_attn_forward(torch.from_numpy(rp).to(DEV), torch.from_numpy(x).to(DEV),
                            torch.from_numpy(wt).to(DEV), heads, 10, ws=ws)
     assert nga.sync_status(ws) == -4
 
 
-@pytest.mark.parametrize("dtype,heads", PATH_CASES)
-def test_order_out_of_range_is_reported(dtype, heads):
+@pytest.mark.parametrize("dtype,c,heads,variant", PATH_CASES)
+def test_order_out_of_range_is_reported(dtype, c, heads, variant):
+    _path_check(dtype, c, heads, 8, variant)
     rp = np.array([0, 4, 8], np.int64)
-    x = W.make_features(8, 16, 1, dtype)
-    wt = W.make_weights(1, 16, 2, dtype)
+    x = W.make_features(8, c, 1, dtype)
+    wt = W.make_weights(1, c, 2, dtype)
     order = torch.tensor([0, 1, 2, 3, 4, 5, 6, 99], dtype=torch.int32, device=DEV)
     ws = nga.Workspace(DEV)
     nga.block_attn_forward(torch.from_numpy(rp).to(DEV), torch.from_numpy(x).to(DEV),

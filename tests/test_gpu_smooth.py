@@ -1,7 +1,7 @@
 """GPU smooth attention (per-segment softmax rescale by sum_j e_j / D~) against the oracle.
 
-Every kernel path the dispatcher can take -- the fused fp32 kernel, the fp64 matrix-core
-path and the generic path in both precisions -- against oracle.attn_smooth, normwise
+Every kernel path the dispatcher can take -- the fused fp32 and fp64 kernels, the fp64
+matrix-core path and the generic path in both precisions -- against oracle.attn_smooth, normwise
 (1e-12 fp64 / 2e-5 fp32), over several layers, with ln D~ drawn per layer, edge and head.
 Plus: ln D~ equal to each segment's log-sum-exp reproduces the vanilla forward; the `order`
 permutation keys ln D~ by edge row; factors far from one (e^-60 .. e^60, differing between the
@@ -79,7 +79,8 @@ CASES = [
     (np.float32, 40, 96, 32, 2, 3, 2, "fused_f32_d16"),
     (np.float32, 30, 40, 16, 1, 1, 3, "fused_f32_d16"),
     (np.float64, 30, 120, 128, 4, 2, 4, "mfma_f64"),
-    (np.float64, 40, 40, 32, 4, 2, 5, "mfma_f64"),
+    (np.float64, 40, 40, 32, 4, 2, 5, "fused_f64"),
+    (np.float64, 30, 90, 64, 4, 2, 8, "mfma_f64"),
     (np.float64, 20, 30, 20, 2, 2, 6, "generic_f64"),
     (np.float32, 20, 60, 40, 5, 2, 7, "generic_f32"),
 ]
@@ -107,7 +108,7 @@ def test_smooth_matches_oracle(oracle_mod, dtype, nc, maxlen, c, heads, layers, 
 
 
 @pytest.mark.parametrize("dtype,c,heads,cap", [(np.float32, 64, 4, 181), (np.float64, 32, 4, 60),
-                                               (np.float64, 20, 2, 40)])
+                                               (np.float64, 64, 4, 90), (np.float64, 20, 2, 40)])
 def test_dtilde_equal_to_segment_sum_is_vanilla(dtype, c, heads, cap):
     rp = W.random_rows(30, cap, 11, min_len=1)
     e = int(rp[-1])
