@@ -392,7 +392,10 @@ int nga_sync_status(void* ws, void* stream);
 const char* nga_strerror(int status);
 
 /* Name of the attention kernel block_attn_forward would launch for these
- * shapes ("fused_f32_d16", "generic", ...), for reporting; never NULL. */
+ * shapes, for reporting; never NULL: "fused_f32_d16" (fp32, 16-wide heads,
+ * rows <= 192), "fused_f64" (fp64, c <= 32, heads of 8 or 16, rows <= 64),
+ * "mfma_f64" (fp64, heads of 8, 16 or 32, rows <= 128), "generic_f32",
+ * "generic_f64", or "unsupported" for an unknown dtype. */
 const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads);
 
 #ifdef __cplusplus
