@@ -82,9 +82,13 @@ def source_digest(paths) -> str:
 
 def attention_sources(variant: str):
     base = "neighbour_graph_attention_amd/csrc/"
-    if variant.startswith("fused"):
+    if variant.startswith("fused_f32"):
         return [base + "block_attn_fused.hip", base + "block_attn_fused.h"]
-    return [base + "block_attn.hip"]
+    if variant == "fused_f64":
+        return [base + "block_attn_f64_fused.hip", base + "block_attn_f64.h"]
+    if variant == "mfma_f64":
+        return [base + "block_attn_f64.hip", base + "block_attn_f64.h"]
+    return [base + "block_attn.hip", base + "gemm_rows.h"]
 
 
 def load_traffic(variant: str, workload: str):
