@@ -12,12 +12,13 @@
 //   2. bin: validate each position, cell id, atomic slot within the cell
 //   3. exclusive scan of cell counts -> cell offsets (scan.hip)
 //   4. scatter atoms into cell order (positions copied bit for bit)
-//   5. select: one work-group per (cell, split) with the cell's stencil table in LDS; each
-//      wavefront takes one centre at a time, reads the stencil cells' cell-sorted positions
-//      with coalesced loads, evaluates the fp64 distance of every candidate, compacts the
-//      accepted ones with ballot/mbcnt into a per-wave LDS list, sorts them in registers
-//      (bitonic on the upper 32 bits of the r2 bit pattern, then near-equal runs re-ranked
-//      by the full key (r2, j, shift)) and writes the first min(sel, count) as the row.
+//   5. select: one work-group per (cell, split) with the cell's stencil merged into segments
+//      in LDS; each wavefront takes one centre at a time (about four per work-group and
+//      wavefront), reads the segments' cell-sorted positions with coalesced loads, evaluates
+//      the fp64 distance of every candidate, compacts the accepted ones with ballot/mbcnt into
+//      a per-wave LDS list, sorts them in registers (bitonic on 32-bit words: a distance
+//      class of r2 above the list index, then runs of equal classes re-ranked by the full key
+//      (r2, j, shift)) and writes the first min(sel, count) as the row.
 //
 // The distance is d = (x_j - x_i) + n*L per axis, r2 = (dx*dx + dy*dy) + dz*dz, in IEEE
 // fp64 with contraction disabled in this file, so every accepted r2 is bit-identical to a
