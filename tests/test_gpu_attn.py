@@ -105,6 +105,8 @@ CASES = [
     (np.float64, 30, 50, 16, 1, 3, 20),      # fused fp64, one head of 16
     (np.float64, 20, 64, 8, 1, 2, 21),       # fused fp64, one head of 8
     (np.float64, 20, 65, 32, 4, 2, 22),      # rows past 64: fp64 matrix-core path
+    (np.float32, 20, 192, 64, 4, 2, 23),     # fused fp32 at its 192-row cap (12 full tiles)
+    (np.float32, 20, 192, 16, 1, 1, 24),     # the same with one head
 ]
 
 
