@@ -6,6 +6,7 @@
  *
  *   nl_build            O(N) cell-list neighbour rows under periodic boundaries
  *   nl_refine           the same rows from cached candidate rows (reuse)
+ *   nl_max_displacement the device-side test for that reuse
  *   nl_build_batch      neighbour rows of many structures in one launch sequence
  *   edge_csr            those rows as a destination CSR with image shifts
  *   block_attn_forward  block-dense multi-head attention through the CSR
@@ -13,6 +14,8 @@
  *   local_attn_forward  LocalAtten: one query per centre over its edges
  *   pair_attn_forward   the same attention by the ragged pair-axis route
  *                       (a measured comparator)
+ *   nga_step_graph_*    one step (nl_build, edge_csr, block_attn_forward)
+ *                       captured as a HIP graph
  *
  * Sources (web pages, cited by title and section):
  *   [P1] deepmd-kit issue "perf: DPA4 .pt2 LAMMPS (C++ AOTI) inference 3-6x
@@ -21,18 +24,21 @@
  *   [P2] deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than
  *        dense and OOM-prone -- move to block-dense attention via the
  *        destination CSR".
+ *   [P4] skill page "ml-mlip-nvalchemi" (batched MLIP inference).
  *
  * Conventions shared by every call:
  *   - Pointers are DEVICE pointers unless their name starts with h_ (host).
  *   - `stream` is a hipStream_t passed as void*.  Every call only enqueues
  *     work on that stream and returns; nothing synchronises except where a
  *     host readback is asked for explicitly (edge_csr's h_n_edges,
- *     nga_sync_status) and in the pair-axis comparator, whose declaration
- *     says so.  No call allocates or frees device memory: the caller owns
- *     every buffer, including the workspace, sized by the *_workspace_bytes
- *     queries (pure host arithmetic).  Keeping the data on the GPU from
- *     positions to outputs, with one optional readback, is what [P1]
- *     "Root cause analysis" and "Proposed optimizations" ask for.
+ *     nga_sync_status) and in nl_build_batch and the pair-axis comparator,
+ *     whose declarations say so.  No call allocates or frees device buffers:
+ *     the caller owns every buffer, including the workspace, sized by the
+ *     *_workspace_bytes queries (pure host arithmetic); only the step-graph
+ *     calls create HIP runtime objects (a stream and a graph).  Keeping the
+ *     data on the GPU from positions to outputs, with one optional readback,
+ *     is what [P1] "Root cause analysis" and "Proposed optimizations" ask
+ *     for.
  *   - Arguments are checked on the host before any HIP call; a bad argument
  *     returns NGA_EINVAL (or NGA_EDTYPE / NGA_EWORKSPACE) and enqueues
  *     nothing.  Errors found by the kernels (a position outside the box, a
@@ -359,8 +365,9 @@ int pair_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
  * the per-kernel launch overhead).  Arguments are those of the three calls;
  * every pointer is baked into the graph, so a replay reads the positions,
  * features and weights those buffers hold at replay time and writes the same
- * outputs; h_box and the other scalars are taken at capture.  Arguments are checked as the calls check them (the error code of
- * the first failing call is returned and no graph is made).  The capture
+ * outputs; h_box and the other scalars are taken at capture.  Arguments are
+ * checked as the calls check them (the error code of the first failing call
+ * is returned and no graph is made).  The capture
  * runs on a stream of its own; nothing is launched.  On success *graph_out
  * receives an opaque handle, to be released with nga_step_graph_destroy.
  * Creating a graph allocates host-side and runtime graph objects (no device
