@@ -772,6 +772,8 @@ struct RefineArgs {
 // positions, those within rcut compacted into the wave's LDS list with ballot / mbcnt, then
 // the same ranking and row write as nl_build (sort_and_write), so that the row equals the one
 // nl_build makes from the same positions whenever the candidates hold every pair within rcut.
+constexpr int kRefineChunks = 4;
+
 __global__ void __launch_bounds__(kNlBlock) refine_kernel(RefineArgs A) {
     __shared__ WaveList lists[kNlWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -787,35 +789,57 @@ __global__ void __launch_bounds__(kNlBlock) refine_kernel(RefineArgs A) {
     const int32_t* csh = A.cshift + (int64_t)i * A.csel * 3;
     bool bad = false;
     int count = 0;
-    for (int t0 = 0; t0 < cn; t0 += 64) {
-        const int t = t0 + lane;
-        bool accept = false;
-        double r2 = 0.0;
-        int j = 0, code = 0;
-        if (t < cn) {
-            j = crow[t];
-            const int nx = csh[3 * t], ny = csh[3 * t + 1], nz = csh[3 * t + 2];
-            if (j >= 0 && j < A.n && nx >= -127 && nx <= 127 && ny >= -127 && ny <= 127 &&
-                nz >= -127 && nz <= 127) {
-                const double dx = (A.pos[3 * (int64_t)j] - xi) + (double)nx * A.L[0];
-                const double dy = (A.pos[3 * (int64_t)j + 1] - yi) + (double)ny * A.L[1];
-                const double dz = (A.pos[3 * (int64_t)j + 2] - zi) + (double)nz * A.L[2];
-                const double sxy = dx * dx + dy * dy;
-                r2 = sxy + dz * dz;
-                accept = r2 < A.rc2 && !(j == i && nx == 0 && ny == 0 && nz == 0);
-                code = pack_shift(nx, ny, nz);
-            } else if (j >= 0) {
-                bad = true;
+    // Rounds of kRefineChunks chunks of 64 candidates: every row entry, then every position
+    // gather of the round is issued before the first distance is evaluated.
+    for (int t0 = 0; t0 < cn; t0 += 64 * kRefineChunks) {
+        int jj[kRefineChunks], sx[kRefineChunks], sy[kRefineChunks], sz[kRefineChunks];
+        bool ok[kRefineChunks];
+#pragma unroll
+        for (int u = 0; u < kRefineChunks; ++u) {
+            const int t = t0 + 64 * u + lane;
+            jj[u] = -1;
+            sx[u] = sy[u] = sz[u] = 0;
+            if (t < cn) {
+                jj[u] = crow[t];
+                sx[u] = csh[3 * t];
+                sy[u] = csh[3 * t + 1];
+                sz[u] = csh[3 * t + 2];
             }
         }
-        const uint64_t m = __ballot(accept);
-        const int slot = count + __popcll(m & lt_mask);
-        if (accept) {
-            L.r2[slot] = (uint64_t)__double_as_longlong(r2);
-            L.j[slot] = j;
-            L.code[slot] = code;
+        double px[kRefineChunks], py[kRefineChunks], pz[kRefineChunks];
+#pragma unroll
+        for (int u = 0; u < kRefineChunks; ++u) {
+            const int j = jj[u];
+            ok[u] = j >= 0 && j < A.n && sx[u] >= -127 && sx[u] <= 127 && sy[u] >= -127 &&
+                    sy[u] <= 127 && sz[u] >= -127 && sz[u] <= 127;
+            if (j >= 0 && !ok[u]) bad = true;
+            const int64_t jp = ok[u] ? j : i;
+            px[u] = A.pos[3 * jp];
+            py[u] = A.pos[3 * jp + 1];
+            pz[u] = A.pos[3 * jp + 2];
         }
-        count += __popcll(m);
+#pragma unroll
+        for (int u = 0; u < kRefineChunks; ++u) {
+            if (t0 + 64 * u >= cn) break;  // uniform
+            bool accept = false;
+            double r2 = 0.0;
+            if (ok[u]) {
+                const double dx = (px[u] - xi) + (double)sx[u] * A.L[0];
+                const double dy = (py[u] - yi) + (double)sy[u] * A.L[1];
+                const double dz = (pz[u] - zi) + (double)sz[u] * A.L[2];
+                const double sxy = dx * dx + dy * dy;
+                r2 = sxy + dz * dz;
+                accept = r2 < A.rc2 && !(jj[u] == i && sx[u] == 0 && sy[u] == 0 && sz[u] == 0);
+            }
+            const uint64_t m = __ballot(accept);
+            const int slot = count + __popcll(m & lt_mask);
+            if (accept) {
+                L.r2[slot] = (uint64_t)__double_as_longlong(r2);
+                L.j[slot] = jj[u];
+                L.code[slot] = pack_shift(sx[u], sy[u], sz[u]);
+            }
+            count += __popcll(m);
+        }
     }
     wave_sync_lds();
     const int keep = count < A.sel ? count : A.sel;
