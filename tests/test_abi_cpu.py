@@ -249,3 +249,28 @@ def test_attention_workspace_and_variant_queries():
     assert nga.attn_variant(L.NGA_F32, 193, 64, 4) == "generic_f32"    # rows past 192
     assert nga.attn_variant(L.NGA_F32, 60, 40, 5) == "generic_f32"     # head width 8
     assert nga.attn_variant(5, 40, 32, 4) == "unsupported"
+
+
+def test_bench_traffic_lookup_names_each_kernels_sources():
+    """bench.py reads a committed HBM-counter summary only while the attention kernel's source
+    is unchanged: every variant the dispatcher can report maps to files that exist, and each
+    committed summary is used exactly when its recorded hash matches those files (else the
+    bench reports no traffic)."""
+    import json
+
+    import bench
+    variants = {nga.attn_variant(dt, cap, c, h) for dt, cap, c, h in [
+        (L.NGA_F32, 181, 64, 4), (L.NGA_F64, 40, 32, 4), (L.NGA_F64, 120, 128, 4),
+        (L.NGA_F64, 40, 20, 2), (L.NGA_F32, 60, 40, 5)]}
+    assert variants == {"fused_f32_d16", "fused_f64", "mfma_f64", "generic_f64", "generic_f32"}
+    for v in variants:
+        for path in bench.attention_sources(v):
+            assert os.path.exists(os.path.join(bench.ROOT, path)), (v, path)
+    prof = os.path.join(bench.ROOT, "profiles")
+    for name in os.listdir(prof):
+        if name.endswith(".traffic.json"):
+            doc = json.load(open(os.path.join(prof, name)))
+            assert doc["source_files"] == bench.attention_sources(doc["kernel"])
+            fresh = doc["source_sha256"] == bench.source_digest(doc["source_files"])
+            expect = doc["hbm_bytes_per_launch"] if fresh else None
+            assert bench.load_traffic(doc["kernel"], doc["workload"]) == expect, name
