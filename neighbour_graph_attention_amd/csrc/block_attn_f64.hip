@@ -176,6 +176,7 @@ __global__ void __launch_bounds__(256) attn_core_f64_kernel(CoreF64Args A) {
         return;
     }
     const int nt = (n + 15) >> 4;
+    const double scale2 = A.scale * kLog2eF64;  // softmax exponents in base 2
     const int c = A.c, c3 = 3 * A.c;
     for (int idx = threadIdx.x; idx < 16 * nt * D; idx += 256) {
         const int b = idx / D, t = idx % D;
@@ -234,7 +235,8 @@ __global__ void __launch_bounds__(256) attn_core_f64_kernel(CoreF64Args A) {
             if (kt < nt) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const double p = exp((s[kt][r] - m) * A.scale);
+                    const bool masked = 16 * kt + gq + 4 * r >= n;
+                    const double p = exp2_nonpos(masked ? -4096.0 : (s[kt][r] - m) * scale2);
                     s[kt][r] = p;
                     z += p;
                 }

@@ -75,6 +75,7 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
     constexpr int C = S::C, CP = S::CP, KC = S::KC, RK = S::RK, UO = S::UO;
     const int g = lane >> 4, l = lane & 15;
     const double scale = 1.0 / __builtin_sqrt((double)D);
+    const double scale2 = scale * kLog2eF64;  // softmax exponents in base 2
 
     // Projection weights of head h: lane (g, l) holds W[4kc+g][hd+l] (zero past the head).
     double wq[KC], wk[KC], wv[KC];
@@ -127,7 +128,8 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const double p = exp((s[kt][r] - m) * scale);
+                const bool masked = 16 * kt + 4 * r + g >= n;
+                const double p = exp2_nonpos(masked ? -4096.0 : (s[kt][r] - m) * scale2);
                 s[kt][r] = p;
                 z += p;
             }
