@@ -427,6 +427,10 @@ def main():
     traffic = load_traffic(variant, w.name)
     nl_bytes = 24.0 * n + 8.0 * (n + 1) + 16.0 * e
     nl_gbs = nl_bytes / ((nl_ms + csr_ms) * 1e-3) / 1e9
+    # edge_csr alone: read each kept row entry (j, 3 shifts) and nnei, write col, shift, dst
+    # and row_ptr.
+    csr_bytes = 16.0 * e + 4.0 * n + 20.0 * e + 8.0 * (n + 1)
+    csr_gbs = csr_bytes / (csr_ms * 1e-3) / 1e9
 
     rec = {
         "metric": METRIC,
@@ -451,6 +455,8 @@ def main():
         "parts_ms": {"nl_build": nl_ms, "edge_csr": csr_ms, "block_attn_forward": attn_ms},
         "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
                    "frac": nl_gbs / PEAK_HBM_GBS},
+        "csr_hbm": {"algorithmic_bytes": csr_bytes, "achieved_gbs": csr_gbs,
+                    "frac": csr_gbs / PEAK_HBM_GBS},
     }
     if graph_rec is not None:
         rec["graph"] = graph_rec
