@@ -15,10 +15,14 @@ LIB = os.path.join(PKG, "libnga.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
-# Packed fp32 VALU instructions are switched off for all device code.
+# Packed fp32 VALU instructions are switched off for all device code.  Matrix-core results
+# stay in ordinary VGPRs: left to its heuristics the compiler keeps the fp64 row GEMM's
+# accumulators in VGPRs across the k loop and copies them to AGPRs and back around every
+# chunk's products (64 extra VALU instructions per 16 MFMAs).
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

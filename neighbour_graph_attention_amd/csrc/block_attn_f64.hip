@@ -71,31 +71,34 @@ __global__ void __launch_bounds__(256) gemm_f64_kernel(GemmF64Args g) {
         for (int j = 0; j < 2; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
 
     // Chunk k0 of A (64 x kKc) and B (kKc x 64) as kPer + kPer values per thread; the next chunk
-    // is loaded into registers while the current one is multiplied out of LDS.
+    // is loaded into registers while the current one is multiplied out of LDS.  A thread reads
+    // the same kPer rows of A (k = k0 + a_kk) and the same column of W (k = k0 + b_k + 4j)
+    // in every chunk, so the row gather and the column offset are resolved once.
+    const int a_kk = tid % kKc, b_k = tid / 64;
+    int64_t a_off[kPer];  // offset of row m0 + tid / kKc + (256 / kKc) j in A, or -1 for zeros
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int64_t m = m0 + tid / kKc + (256 / kKc) * j;
+        a_off[j] = -1;
+        if (m < E) {
+            const int64_t row = g.a_rows ? (int64_t)g.a_rows[m] : m;
+            if (row >= 0 && row < g.n_edges) a_off[j] = row * g.lda;
+            else bad = true;
+        }
+    }
+    const int u = u0 + tid % 64;
+    const bool u_in = u < nout;
+    const double* wcol = g.w + (u_in ? (int64_t)(u / g.c) * g.c * g.c + (u % g.c) : 0);
     double pa[kPer], pb[kPer];
     auto fetch = [&](int k0) {
+        const bool a_k_in = k0 + a_kk < g.c;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+            pa[j] = (a_off[j] >= 0 && a_k_in) ? g.a[a_off[j] + k0 + a_kk] : 0.0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
-            const int idx = tid + 256 * j;
-            const int r = idx / kKc, kk = idx % kKc;
-            const int64_t m = m0 + r;
-            double v = 0.0;
-            if (m < E && k0 + kk < g.c) {
-                const int64_t row = g.a_rows ? (int64_t)g.a_rows[m] : m;
-                if (row >= 0 && row < g.n_edges) v = g.a[row * g.lda + k0 + kk];
-                else bad = true;
-            }
-            pa[j] = v;
-        }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-            const int idx = tid + 256 * j;
-            const int kk = idx / 64, cc = idx % 64;
-            const int u = u0 + cc, t = k0 + kk;
-            double v = 0.0;
-            if (u < nout && t < g.c)
-                v = g.w[(int64_t)(u / g.c) * g.c * g.c + (int64_t)t * g.c + (u % g.c)];
-            pb[j] = v;
+            const int t = k0 + b_k + 4 * j;
+            pb[j] = (u_in && t < g.c) ? wcol[(int64_t)t * g.c] : 0.0;
         }
     };
     fetch(0);
