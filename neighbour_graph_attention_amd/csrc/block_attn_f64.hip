@@ -160,13 +160,102 @@ struct CoreF64Args {
 
 constexpr int kF64TileMax = 8;  // rows per centre up to 128
 
+// The query tiles of wavefront w (w, w + 4, ...) for a centre of NT = ceil(n / 16) key tiles,
+// K and V of head h in sK / sV (rows NT*16 and beyond unused, rows n .. 16 NT - 1 zero).
+template <int D, int NT>
+__device__ __forceinline__ void core_query_tiles(const CoreF64Args& A,
+                                                 const double (*__restrict__ sK)[D + 1],
+                                                 const double (*__restrict__ sV)[D + 1],
+                                                 const int64_t r0, const int n, const int h,
+                                                 const double scale2) {
+    constexpr int KSTEP = (D + 3) / 4;  // k-steps of the score product
+    constexpr int DT = (D + 15) / 16;   // 16-row tiles of O^T
+    const int c = A.c, c3 = 3 * A.c;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int gq = lane >> 4, li = lane & 15;
+    for (int qt = w; qt < NT; qt += 4) {
+        const int a = 16 * qt + li;
+        // Q operand: lane (gq, li) holds Q[a][4kk + gq] for k-step kk.
+        double q[KSTEP];
+#pragma unroll
+        for (int kk = 0; kk < KSTEP; ++kk) {
+            const int t = 4 * kk + gq;
+            q[kk] = (a < n && t < D) ? A.qkv[(r0 + a) * c3 + h * D + t] : 0.0;
+        }
+        d4 s[NT];
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt) {
+            d4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int kk = 0; kk < KSTEP; ++kk) {
+                const int t = 4 * kk + gq;
+                const double kval = t < D ? sK[16 * kt + li][t] : 0.0;
+                acc = mfma64(kval, q[kk], acc);
+            }
+            s[kt] = acc;  // lane (gq, li), register r: key 16kt + gq + 4r, query a
+            // Keeps the scheduler from hoisting every tile's LDS reads at once.
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        double m = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (16 * kt + gq + 4 * r >= n) s[kt][r] = -INFINITY;
+                m = fmax(m, s[kt][r]);
+            }
+        m = fmax(m, __shfl_xor(m, 16, 64));
+        m = fmax(m, __shfl_xor(m, 32, 64));
+        double z = 0.0;
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool masked = 16 * kt + gq + 4 * r >= n;
+                const double p = exp2_nonpos(masked ? -4096.0 : (s[kt][r] - m) * scale2);
+                s[kt][r] = p;
+                z += p;
+            }
+        z += __shfl_xor(z, 16, 64);
+        z += __shfl_xor(z, 32, 64);
+        // Smooth attention: sum_j e_j / D~ times the softmax = exp(s_j - ln D~), i.e. the
+        // weighted sum times exp(m - ln D~) in place of 1/Z.
+        double f = 1.0 / z;
+        if (A.ldt) {
+            f = 0.0;
+            if (a < n) {
+                const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
+                if (row >= 0 && row < A.n_edges)
+                    f = exp(m * A.scale - A.ldt[row * gridDim.y + h]);
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+            d4 acc = {0.0, 0.0, 0.0, 0.0};
+            const int tcol = 16 * dt + li;
+#pragma unroll
+            for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const double vval = tcol < D ? sV[16 * kt + gq + 4 * r][tcol] : 0.0;
+                    acc = mfma64(vval, s[kt][r], acc);
+                    if (r == 3) __builtin_amdgcn_sched_barrier(0);
+                }
+            // lane (gq, li), register r: O[a = 16qt + li][t = 16dt + gq + 4r]
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * dt + gq + 4 * r;
+                if (a < n && t < D) A.o[(r0 + a) * c + h * D + t] = acc[r] * f;
+            }
+        }
+    }
+}
+
 // One work-group per (centre = blockIdx.x, head = blockIdx.y); wave w takes query tiles
 // w, w+4, ...  K_h and V_h of the centre sit in LDS (rows past n are zero).
 template <int D>
-__global__ void __launch_bounds__(256) attn_core_f64_kernel(CoreF64Args A) {
-    constexpr int DP = D + 1;           // padded LDS row (doubles)
-    constexpr int KSTEP = (D + 3) / 4;  // k-steps of the score product
-    constexpr int DT = (D + 15) / 16;   // 16-row tiles of O^T
+__global__ void __launch_bounds__(256, 2) attn_core_f64_kernel(CoreF64Args A) {
+    constexpr int DP = D + 1;  // padded LDS row (doubles)
     __shared__ double sK[16 * kF64TileMax][DP];
     __shared__ double sV[16 * kF64TileMax][DP];
 
@@ -194,89 +283,15 @@ __global__ void __launch_bounds__(256) attn_core_f64_kernel(CoreF64Args A) {
     }
     __syncthreads();
 
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int gq = lane >> 4, li = lane & 15;
-    for (int qt = w; qt < nt; qt += 4) {
-        const int a = 16 * qt + li;
-        // Q operand: lane (gq, li) holds Q[a][4kk + gq] for k-step kk.
-        double q[KSTEP];
-#pragma unroll
-        for (int kk = 0; kk < KSTEP; ++kk) {
-            const int t = 4 * kk + gq;
-            q[kk] = (a < n && t < D) ? A.qkv[(r0 + a) * c3 + h * D + t] : 0.0;
-        }
-        d4 s[kF64TileMax];
-#pragma unroll
-        for (int kt = 0; kt < kF64TileMax; ++kt) {
-            if (kt < nt) {
-                d4 acc = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-                for (int kk = 0; kk < KSTEP; ++kk) {
-                    const int t = 4 * kk + gq;
-                    const double kval = t < D ? sK[16 * kt + li][t] : 0.0;
-                    acc = mfma64(kval, q[kk], acc);
-                }
-                s[kt] = acc;  // lane (gq, li), register r: key 16kt + gq + 4r, query a
-            }
-        }
-        double m = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < kF64TileMax; ++kt) {
-            if (kt < nt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (16 * kt + gq + 4 * r >= n) s[kt][r] = -INFINITY;
-                    m = fmax(m, s[kt][r]);
-                }
-            }
-        }
-        m = fmax(m, __shfl_xor(m, 16, 64));
-        m = fmax(m, __shfl_xor(m, 32, 64));
-        double z = 0.0;
-#pragma unroll
-        for (int kt = 0; kt < kF64TileMax; ++kt) {
-            if (kt < nt) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool masked = 16 * kt + gq + 4 * r >= n;
-                    const double p = exp2_nonpos(masked ? -4096.0 : (s[kt][r] - m) * scale2);
-                    s[kt][r] = p;
-                    z += p;
-                }
-            }
-        }
-        z += __shfl_xor(z, 16, 64);
-        z += __shfl_xor(z, 32, 64);
-        // Smooth attention: sum_j e_j / D~ times the softmax = exp(s_j - ln D~), i.e. the
-        // weighted sum times exp(m - ln D~) in place of 1/Z.
-        double f = 0.0;
-        if (A.ldt && a < n) {
-            const int64_t row = A.order ? (int64_t)A.order[r0 + a] : r0 + a;
-            if (row >= 0 && row < A.n_edges)
-                f = exp(m * A.scale - A.ldt[row * gridDim.y + h]);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            d4 acc = {0.0, 0.0, 0.0, 0.0};
-            const int tcol = 16 * dt + li;
-#pragma unroll
-            for (int kt = 0; kt < kF64TileMax; ++kt) {
-                if (kt < nt) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const double vval = tcol < D ? sV[16 * kt + gq + 4 * r][tcol] : 0.0;
-                        acc = mfma64(vval, s[kt][r], acc);
-                    }
-                }
-            }
-            // lane (gq, li), register r: O[a = 16qt + li][t = 16dt + gq + 4r]
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * dt + gq + 4 * r;
-                if (a < n && t < D)
-                    A.o[(r0 + a) * c + h * D + t] = A.ldt ? acc[r] * f : acc[r] / z;
-            }
-        }
+    switch (nt) {
+        case 1: core_query_tiles<D, 1>(A, sK, sV, r0, n, h, scale2); break;
+        case 2: core_query_tiles<D, 2>(A, sK, sV, r0, n, h, scale2); break;
+        case 3: core_query_tiles<D, 3>(A, sK, sV, r0, n, h, scale2); break;
+        case 4: core_query_tiles<D, 4>(A, sK, sV, r0, n, h, scale2); break;
+        case 5: core_query_tiles<D, 5>(A, sK, sV, r0, n, h, scale2); break;
+        case 6: core_query_tiles<D, 6>(A, sK, sV, r0, n, h, scale2); break;
+        case 7: core_query_tiles<D, 7>(A, sK, sV, r0, n, h, scale2); break;
+        default: core_query_tiles<D, 8>(A, sK, sV, r0, n, h, scale2); break;
     }
 }
 
