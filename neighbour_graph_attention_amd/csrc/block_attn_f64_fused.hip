@@ -77,14 +77,24 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
     const double scale = 1.0 / __builtin_sqrt((double)D);
     const double scale2 = scale * kLog2eF64;  // softmax exponents in base 2
 
-    // Projection weights of head h: lane (g, l) holds W[4kc+g][hd+l] (zero past the head).
+    // Projections of head h.  Heads of 16: lane (g, l) holds W[4kc+g][hd+l] of Wq, Wk and Wv,
+    // and Q^T, K^T, V take one product each.  Heads of 8 would leave half of every 16-row
+    // Q^T and K^T tile empty, so Q^T and K^T share one: A rows 0..7 are Wq's head columns and
+    // rows 8..15 Wk's, which puts Q^T channel 4r+g in registers r = 0, 1 and K^T channel
+    // 4(r-2)+g in registers 2, 3 (V keeps 8 of its 16 columns).
+    constexpr bool kStackQK = D == 8;
     double wq[KC], wk[KC], wv[KC];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-        const int idx = (4 * kc + g) * C + h * D + l;
+        const int idx = (4 * kc + g) * C + h * D + (kStackQK ? (l & 7) : l);
         const bool in_head = l < D;
-        wq[kc] = in_head ? W[idx] : 0.0;
-        wk[kc] = in_head ? W[C * C + idx] : 0.0;
+        if constexpr (kStackQK) {
+            wq[kc] = in_head ? W[idx] : W[C * C + idx];
+            wk[kc] = 0.0;
+        } else {
+            wq[kc] = in_head ? W[idx] : 0.0;
+            wk[kc] = in_head ? W[C * C + idx] : 0.0;
+        }
         wv[kc] = in_head ? W[2 * C * C + idx] : 0.0;
     }
     d4 qT[NT], kT[NT], v[NT];
@@ -95,7 +105,7 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
         for (int kc = 0; kc < KC; ++kc) {
             const double xv = sX[(16 * t + l) * CP + 4 * kc + g];
             q = mfma64(wq[kc], xv, q);
-            k = mfma64(wk[kc], xv, k);
+            if constexpr (!kStackQK) k = mfma64(wk[kc], xv, k);
             vv = mfma64(xv, wv[kc], vv);
         }
         qT[t] = q;
@@ -110,7 +120,10 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
         for (int kt = 0; kt < NT; ++kt) {
             d4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-            for (int r = 0; r < RK; ++r) acc = mfma64(kT[kt][r], qT[qt][r], acc);
+            for (int r = 0; r < RK; ++r) {
+                if constexpr (kStackQK) acc = mfma64(qT[kt][2 + r], qT[qt][r], acc);
+                else acc = mfma64(kT[kt][r], qT[qt][r], acc);
+            }
             s[kt] = acc;
         }
         double m = -INFINITY;
