@@ -167,9 +167,11 @@ struct CoreF64Args {
 };
 
 constexpr int kF64TileMax = 8;  // rows per centre up to 128
+constexpr int kCoreWaves = 8;   // wavefronts per attention-core work-group
 
-// The query tiles of wavefront w (w, w + 4, ...) for a centre of NT = ceil(n / 16) key tiles,
-// K and V of head h in sK / sV (rows NT*16 and beyond unused, rows n .. 16 NT - 1 zero).
+// The query tiles of wavefront w (w, w + kCoreWaves, ...) for a centre of NT = ceil(n / 16)
+// key tiles, K and V of head h in sK / sV (rows NT*16 and beyond unused, rows n .. 16 NT - 1
+// zero).
 template <int D, int NT>
 __device__ __forceinline__ void core_query_tiles(const CoreF64Args& A,
                                                  const double (*__restrict__ sK)[D + 1],
@@ -181,7 +183,7 @@ __device__ __forceinline__ void core_query_tiles(const CoreF64Args& A,
     const int c = A.c, c3 = 3 * A.c;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int gq = lane >> 4, li = lane & 15;
-    for (int qt = w; qt < NT; qt += 4) {
+    for (int qt = w; qt < NT; qt += kCoreWaves) {
         const int a = 16 * qt + li;
         // Q operand: lane (gq, li) holds Q[a][4kk + gq] for k-step kk.
         double q[KSTEP];
@@ -259,10 +261,12 @@ __device__ __forceinline__ void core_query_tiles(const CoreF64Args& A,
     }
 }
 
-// One work-group per (centre = blockIdx.x, head = blockIdx.y); wave w takes query tiles
-// w, w+4, ...  K_h and V_h of the centre sit in LDS (rows past n are zero).
+// One work-group per (centre = blockIdx.x, head = blockIdx.y) of kCoreWaves wavefronts; wave w
+// takes query tiles w, w + kCoreWaves, ...  K_h and V_h of the centre sit in LDS (rows past n
+// are zero).  Eight wavefronts of at most 128 VGPRs give four per SIMD, twice what four
+// wavefronts per work-group reached.
 template <int D>
-__global__ void __launch_bounds__(256, 2) attn_core_f64_kernel(CoreF64Args A) {
+__global__ void __launch_bounds__(64 * kCoreWaves, 2) attn_core_f64_kernel(CoreF64Args A) {
     constexpr int DP = D + 1;  // padded LDS row (doubles)
     __shared__ double sK[16 * kF64TileMax][DP];
     __shared__ double sV[16 * kF64TileMax][DP];
@@ -278,7 +282,7 @@ __global__ void __launch_bounds__(256, 2) attn_core_f64_kernel(CoreF64Args A) {
     const int nt = (n + 15) >> 4;
     const double scale2 = A.scale * kLog2eF64;  // softmax exponents in base 2
     const int c = A.c, c3 = 3 * A.c;
-    for (int idx = threadIdx.x; idx < 16 * nt * D; idx += 256) {
+    for (int idx = threadIdx.x; idx < 16 * nt * D; idx += 64 * kCoreWaves) {
         const int b = idx / D, t = idx % D;
         double kv = 0.0, vv = 0.0;
         if (b < n) {
@@ -316,7 +320,7 @@ int launch_gemm(const GemmF64Args& g, int64_t m_bound, hipStream_t s) {
 }
 
 int launch_core(const CoreF64Args& a, int64_t n_centres, int heads, int d, hipStream_t s) {
-    dim3 grid((unsigned)n_centres, (unsigned)heads), block(256);
+    dim3 grid((unsigned)n_centres, (unsigned)heads), block(64 * kCoreWaves);
     if (d == 8) hipLaunchKernelGGL(attn_core_f64_kernel<8>, grid, block, 0, s, a);
     else if (d == 16) hipLaunchKernelGGL(attn_core_f64_kernel<16>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(attn_core_f64_kernel<32>, grid, block, 0, s, a);
