@@ -273,6 +273,20 @@ __device__ inline uint32_t dist_class(uint64_t r2_bits, double qscale) {
     return s < kClassMax ? (uint32_t)s : (uint32_t)kClassMax;
 }
 
+// v of lane (this lane xor lx), lx a power of two below 64: lane-local DPP moves within a quad
+// for 1 and 2, an LDS-free swizzle within 32 lanes for 4 to 16, a permute for 32.  The sort
+// below is a chain of such exchanges, so their latency adds up.
+__device__ inline uint32_t xor_lanes(uint32_t v, int lx) {
+    switch (lx) {
+        case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+        case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+        case 4: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);
+        case 8: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (8 << 10) | 0x1F);
+        case 16: return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (16 << 10) | 0x1F);
+        default: return __shfl_xor(v, lx, 64);
+    }
+}
+
 // Bitonic sort of 64*NS 32-bit words held NS per lane (element e = lane*NS + q), ascending.
 template <int NS>
 __device__ inline void bitonic_sort(uint32_t (&k)[NS], int lane) {
@@ -297,7 +311,7 @@ __device__ inline void bitonic_sort(uint32_t (&k)[NS], int lane) {
 #pragma unroll
                 for (int q = 0; q < NS; ++q) {
                     const int e = lane * NS + q;
-                    const uint32_t ok = __shfl_xor(k[q], lx, 64);
+                    const uint32_t ok = xor_lanes(k[q], lx);
                     const bool ascending = (e & size) == 0;
                     const bool lower = (e & stride) == 0;
                     k[q] = lower == ascending ? min(ok, k[q]) : max(ok, k[q]);
