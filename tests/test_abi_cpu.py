@@ -274,3 +274,17 @@ def test_bench_traffic_lookup_names_each_kernels_sources():
             fresh = doc["source_sha256"] == bench.source_digest(doc["source_files"])
             expect = doc["hbm_bytes_per_launch"] if fresh else None
             assert bench.load_traffic(doc["kernel"], doc["workload"]) == expect, name
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus above 1 exits with status 2 and says so, before it
+    touches a device."""
+    import subprocess
+    import sys
+
+    import bench
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
