@@ -198,6 +198,94 @@ scatter_kernel(const double* __restrict__ pos, int n, const int64_t* __restrict_
     sidx[d] = i;
 }
 
+// Small systems: counting, the exclusive scan of the cell counts and the scatter in one
+// work-group, with the counts in LDS, in place of five launches (clear, bin, two scan
+// passes, scatter) that each cost more in launch latency than in work.  The order of atoms
+// inside a cell differs from the multi-launch path, as it does between any two runs of that
+// path's atomics; rows do not depend on it, since each row is sorted by its full key.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallPer = 8;                            // atoms per thread
+constexpr int kSmallAtoms = kSmallThreads * kSmallPer;  // 8,192
+constexpr int kSmallCells = 4096;
+
+__global__ void __launch_bounds__(kSmallThreads)
+bin_small_kernel(const double* __restrict__ pos, int n, Geom g, int64_t* __restrict__ cell_start,
+                 double* __restrict__ sx, double* __restrict__ sy, double* __restrict__ sz,
+                 int32_t* __restrict__ sidx, uint32_t* status) {
+    __shared__ int32_t s_count[kSmallCells];
+    __shared__ int32_t s_wave[kSmallThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nc = (int)g.ncells;
+    for (int c = tid; c < nc; c += kSmallThreads) s_count[c] = 0;
+    __syncthreads();
+
+    int cell[kSmallPer], slot[kSmallPer];
+    bool bad = false;
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        const int i = tid + kSmallThreads * k;
+        cell[k] = 0;
+        slot[k] = 0;
+        if (i < n) {
+            int c[3];
+            for (int a = 0; a < 3; ++a) {
+                const double x = pos[3 * (int64_t)i + a];
+                // NaN and +-inf fail one of the two comparisons.
+                const bool ok = (x >= 0.0) && (x < g.L[a]);
+                bad |= !ok;
+                const int ci = ok ? (int)(x * g.inv_h[a]) : 0;
+                c[a] = ci < g.nc[a] ? ci : g.nc[a] - 1;
+            }
+            cell[k] = (c[2] * g.nc[1] + c[1]) * g.nc[0] + c[0];
+            slot[k] = atomicAdd(&s_count[cell[k]], 1);
+        }
+    }
+    if (bad) raise_bits(status, kBitBox);
+    __syncthreads();
+
+    // Exclusive scan: thread t owns cells t*per .. t*per + per - 1.
+    const int per = (nc + kSmallThreads - 1) / kSmallThreads;
+    const int c0 = tid * per;
+    int mine = 0;
+    for (int j = 0; j < per; ++j)
+        if (c0 + j < nc) mine += s_count[c0 + j];
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int run = incl - mine, total = 0;
+    for (int w = 0; w < kSmallThreads / 64; ++w) {
+        if (w < wave) run += s_wave[w];
+        total += s_wave[w];
+    }
+    for (int j = 0; j < per; ++j) {
+        if (c0 + j < nc) {
+            const int cnt = s_count[c0 + j];
+            cell_start[c0 + j] = run;
+            s_count[c0 + j] = run;  // this thread's own cells only
+            run += cnt;
+        }
+    }
+    if (tid == 0) cell_start[nc] = total;
+    __syncthreads();
+
+#pragma unroll
+    for (int k = 0; k < kSmallPer; ++k) {
+        const int i = tid + kSmallThreads * k;
+        if (i < n) {
+            const int d = s_count[cell[k]] + slot[k];
+            sx[d] = pos[3 * (int64_t)i + 0];
+            sy[d] = pos[3 * (int64_t)i + 1];
+            sz[d] = pos[3 * (int64_t)i + 2];
+            sidx[d] = i;
+        }
+    }
+}
+
 // Image shift n packed 8 bits per axis with offset 128: code = (nx+128)<<16 | (ny+128)<<8 |
 // (nz+128).  Ordering codes as integers orders shifts lexicographically (nx, ny, nz).
 __device__ inline int pack_shift(int nx, int ny, int nz) {
@@ -613,17 +701,24 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     WsLayout w = carve(ws, n, g);
     uint32_t* status = &static_cast<WsHeader*>(ws)->status;
     const int ni = (int)n;
-    hipLaunchKernelGGL(clear_i32_kernel, dim3((unsigned)((g.ncells + 255) / 256)), dim3(256), 0,
-                       s, w.cell_count, g.ncells);
-    hipLaunchKernelGGL(bin_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni, g,
-                       w.cell_count, w.atom_cell, w.atom_slot, status);
-    int rc = last_launch_status();
-    if (rc) return rc;
-    if ((rc = scan_counts_tile_sums(w.cell_count, g.ncells, w.tile_sums, s))) return rc;
-    if ((rc = scan_counts_finish(w.cell_count, g.ncells, w.tile_sums, w.cell_start, s))) return rc;
-    hipLaunchKernelGGL(scatter_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,
-                       w.cell_start, w.atom_cell, w.atom_slot, w.sx, w.sy, w.sz, w.sidx);
-    if ((rc = last_launch_status())) return rc;
+    int rc;
+    if (n <= kSmallAtoms && g.ncells <= kSmallCells) {
+        hipLaunchKernelGGL(bin_small_kernel, dim3(1), dim3(kSmallThreads), 0, s, pos, ni, g,
+                           w.cell_start, w.sx, w.sy, w.sz, w.sidx, status);
+        if ((rc = last_launch_status())) return rc;
+    } else {
+        hipLaunchKernelGGL(clear_i32_kernel, dim3((unsigned)((g.ncells + 255) / 256)), dim3(256),
+                           0, s, w.cell_count, g.ncells);
+        hipLaunchKernelGGL(bin_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni, g,
+                           w.cell_count, w.atom_cell, w.atom_slot, status);
+        if ((rc = last_launch_status())) return rc;
+        if ((rc = scan_counts_tile_sums(w.cell_count, g.ncells, w.tile_sums, s))) return rc;
+        if ((rc = scan_counts_finish(w.cell_count, g.ncells, w.tile_sums, w.cell_start, s)))
+            return rc;
+        hipLaunchKernelGGL(scatter_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,
+                           w.cell_start, w.atom_cell, w.atom_slot, w.sx, w.sy, w.sz, w.sidx);
+        if ((rc = last_launch_status())) return rc;
+    }
 
     SelectArgs A;
     A.g = g;
