@@ -8,7 +8,8 @@
 // the destination CSR (destination_row_ptr) that the attention gathers through.
 //
 // Three launches: per-row edge counts (+ per-tile sums), tile scan into row_ptr, and a
-// fill where one wavefront compacts one row with ballot/mbcnt, keeping slot order.
+// fill where one wavefront compacts one row with ballot/mbcnt, keeping slot order.  Up to
+// 8,192 rows with nnei given, one work-group does the counts and the scan.
 #pragma clang fp contract(off)
 
 #include "nga_internal.h"
@@ -52,6 +53,52 @@ count_kernel(const int32_t* __restrict__ nbr, const int32_t* __restrict__ nnei, 
         }
     }
     if (lane == 0) counts[row] = cnt;
+}
+
+// Small inputs with nnei given: the row counts and their exclusive scan in one work-group,
+// in place of three launches (counts, tile sums, tile scan).
+constexpr int kSmallCsrThreads = 1024;
+constexpr int kSmallCsrPer = 8;  // rows per thread, contiguous
+constexpr int kSmallCsrRows = kSmallCsrThreads * kSmallCsrPer;
+
+__global__ void __launch_bounds__(kSmallCsrThreads)
+row_ptr_small_kernel(const int32_t* __restrict__ nnei, int n, int sel,
+                     int64_t* __restrict__ row_ptr) {
+    __shared__ int32_t s_wave[kSmallCsrThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int cnt[kSmallCsrPer];
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < kSmallCsrPer; ++j) {
+        const int row = tid * kSmallCsrPer + j;
+        int c = 0;
+        if (row < n) {
+            const int v = nnei[row];
+            c = v < 0 ? 0 : (v < sel ? v : sel);
+        }
+        cnt[j] = c;
+        mine += c;
+    }
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_wave[wave] = incl;
+    __syncthreads();
+    int64_t run = incl - mine, total = 0;
+    for (int w = 0; w < kSmallCsrThreads / 64; ++w) {
+        if (w < wave) run += s_wave[w];
+        total += s_wave[w];
+    }
+#pragma unroll
+    for (int j = 0; j < kSmallCsrPer; ++j) {
+        const int row = tid * kSmallCsrPer + j;
+        if (row < n) row_ptr[row] = run;
+        run += cnt[j];
+    }
+    if (tid == 0) row_ptr[n] = total;
 }
 
 struct FillArgs {
@@ -180,11 +227,17 @@ extern "C" int edge_csr(const int32_t* nbr, const int32_t* nbr_shift, const int3
         if ((rc = last_launch_status())) return rc;
     } else {
         const unsigned blocks = (unsigned)(((int64_t)n * 64 + 255) / 256);
-        hipLaunchKernelGGL(count_kernel, dim3(blocks), dim3(256), 0, s, nbr, nnei, n, sel,
-                           w.counts);
-        if ((rc = last_launch_status())) return rc;
-        if ((rc = scan_counts_tile_sums(w.counts, n, w.tile_sums, s))) return rc;
-        if ((rc = scan_counts_finish(w.counts, n, w.tile_sums, row_ptr, s))) return rc;
+        if (nnei && n <= kSmallCsrRows) {
+            hipLaunchKernelGGL(row_ptr_small_kernel, dim3(1), dim3(kSmallCsrThreads), 0, s, nnei,
+                               n, sel, row_ptr);
+            if ((rc = last_launch_status())) return rc;
+        } else {
+            hipLaunchKernelGGL(count_kernel, dim3(blocks), dim3(256), 0, s, nbr, nnei, n, sel,
+                               w.counts);
+            if ((rc = last_launch_status())) return rc;
+            if ((rc = scan_counts_tile_sums(w.counts, n, w.tile_sums, s))) return rc;
+            if ((rc = scan_counts_finish(w.counts, n, w.tile_sums, row_ptr, s))) return rc;
+        }
         FillArgs A;
         A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
         A.n = n; A.sel = sel; A.pos = pos;
