@@ -286,11 +286,7 @@ int attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order, int64_
         return run_fused_f64(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
                              static_cast<const double*>(weights), static_cast<const double*>(x),
                              static_cast<const double*>(ldt), static_cast<double*>(y), status, s);
-    hipLaunchKernelGGL(check_rows_kernel, dim3(1), dim3(1), 0, s, row_ptr, (int)n_centres, n_edges,
-                       status);
-    int rc = last_launch_status();
-    if (rc) return rc;
-    if (dtype == NGA_F64 && f64_mfma_supported(nnei_cap, c, n_heads)) {
+    if (dtype == NGA_F64 && f64_mfma_supported(nnei_cap, c, n_heads)) {  // its core checks row_ptr
         GenericWs w = carve_generic(ws, n_edges, c, n_layers, sizeof(double));
         return run_f64_mfma(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
                             static_cast<const double*>(weights), static_cast<const double*>(x),
@@ -298,6 +294,9 @@ int attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order, int64_
                             static_cast<double*>(w.qkv),
                             static_cast<double*>(w.o), static_cast<double*>(w.xbuf), status, s);
     }
+    hipLaunchKernelGGL(check_rows_kernel, dim3(1), dim3(1), 0, s, row_ptr, (int)n_centres, n_edges,
+                       status);
+    if (int rc = last_launch_status()) return rc;
     if (dtype == NGA_F64)
         return run_generic<double>(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads,
                                    n_layers, static_cast<const double*>(weights),

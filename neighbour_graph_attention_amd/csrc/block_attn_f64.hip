@@ -157,6 +157,7 @@ struct CoreF64Args {
     const double* qkv;  // [E][3c] slot-indexed: q | k | v
     double* o;          // [E][c] slot-indexed
     const int64_t* row_ptr;
+    int64_t n_centres;
     int64_t n_edges;
     int nnei_cap;
     int c;
@@ -272,6 +273,10 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 2) attn_core_f64_kernel(CoreF
     __shared__ double sV[16 * kF64TileMax][DP];
 
     const int centre = blockIdx.x, h = blockIdx.y;
+    // The CSR as a whole: it starts at 0 and ends within the edge rows.
+    if (centre == 0 && h == 0 && threadIdx.x == 0) {
+        if (A.row_ptr[0] != 0 || A.row_ptr[A.n_centres] > A.n_edges) raise_bits(A.status, kBitCap);
+    }
     const int64_t r0 = A.row_ptr[centre], r1 = A.row_ptr[centre + 1];
     const int n = (int)(r1 - r0);
     if (n <= 0) return;
@@ -364,6 +369,7 @@ int run_f64_mfma(const int64_t* row_ptr, const int32_t* order, int64_t n_centres
         a.qkv = qkv;
         a.o = o;
         a.row_ptr = row_ptr;
+        a.n_centres = n_centres;
         a.n_edges = n_edges;
         a.nnei_cap = nnei_cap;
         a.c = c;
