@@ -504,7 +504,7 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, double
 // loads, testing the pinned fp64 distance and compacting the accepted candidates into its
 // LDS list with ballot / mbcnt.
 // BATCH: the cells of several structures, each block finding its structure's geometry.
-template <bool BATCH>
+template <bool BATCH, bool FLAT>
 __global__ void __launch_bounds__(kNlBlock)
 select_kernel(SelectArgs A) {
     const int gcell = blockIdx.x;
@@ -622,7 +622,58 @@ select_kernel(SelectArgs A) {
         const int i = sidx[ci];
         const double xi = sx[ci], yi = sy[ci], zi = sz[ci];
         int count = 0;
-        for (int sc = 0; sc < nseg; ++sc) {
+        if constexpr (FLAT) {
+            // Short segments (small boxes, where most of the stencil is periodic images, or few
+            // atoms per cell): rounds of three 64-candidate chunks taken across segment ends,
+            // each chunk with its own image shift, instead of whole rounds per segment.
+            int sc = 0, off = 0;
+            while (sc < nseg) {  // uniform
+                double cx[3], cy[3], cz[3];
+                int cj[3], cl[3], cc[3];
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    cl[u] = 0;
+                    cc[u] = zero_code;
+                    if (sc < nseg) {  // uniform
+                        const int len = s_len[sc];
+                        cl[u] = len - off < 64 ? len - off : 64;
+                        cc[u] = s_code[sc];
+                        const int a = s_start[sc] + off + (lane < cl[u] ? lane : 0);
+                        cx[u] = sx[a];
+                        cy[u] = sy[a];
+                        cz[u] = sz[a];
+                        cj[u] = sidx[a];
+                        off += 64;
+                        if (off >= len) {
+                            ++sc;
+                            off = 0;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    if (cl[u] == 0) break;  // uniform
+                    const int code = cc[u];
+                    const double dx = (cx[u] - xi) + (double)shift_x(code) * Lx;
+                    const double dy = (cy[u] - yi) + (double)shift_y(code) * Ly;
+                    const double dz = (cz[u] - zi) + (double)shift_z(code) * Lz;
+                    const double sxy = dx * dx + dy * dy;
+                    const double r2 = sxy + dz * dz;
+                    const int j = cj[u];
+                    const bool accept =
+                        lane < cl[u] && (r2 < rc2) && !(j == i && code == zero_code);
+                    const uint64_t m = __ballot(accept);
+                    const int slot = count + __popcll(m & lt_mask);
+                    if (accept && slot < NGA_ROW_CAP) {
+                        L.r2[slot] = (uint64_t)__double_as_longlong(r2);
+                        L.j[slot] = j;
+                        L.code[slot] = code;
+                    }
+                    count += __popcll(m);
+                }
+            }
+        }
+        for (int sc = 0; sc < (FLAT ? 0 : nseg); ++sc) {
             const int base = s_start[sc], len = s_len[sc], code = s_code[sc];
             const double nx = (double)shift_x(code) * Lx;
             const double ny = (double)shift_y(code) * Ly;
@@ -733,8 +784,18 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     A.table = nullptr;
     A.cell_ptr = nullptr;
     A.n_structs = 1;
-    hipLaunchKernelGGL(select_kernel<false>, dim3((unsigned)g.ncells, (unsigned)A.nsplit),
-                       dim3(kNlBlock), (unsigned)select_lds_bytes(g), s, A);
+    // Candidate rounds that cross segment ends pay off when segments are shorter than about a
+    // round and a half: a segment is about one x-row of stencil cells (a single cell when the
+    // box has one cell per row, whose images then come as separate segments).
+    const double seg_est = (double)n / (double)g.ncells *
+                           (double)std::min(g.nc[0], 2 * g.reach[0] + 1);
+    const bool flat = seg_est <= 96.0;
+    if (flat)
+        hipLaunchKernelGGL((select_kernel<false, true>), dim3((unsigned)g.ncells,
+                           (unsigned)A.nsplit), dim3(kNlBlock), (unsigned)select_lds_bytes(g), s, A);
+    else
+        hipLaunchKernelGGL((select_kernel<false, false>), dim3((unsigned)g.ncells,
+                           (unsigned)A.nsplit), dim3(kNlBlock), (unsigned)select_lds_bytes(g), s, A);
     return last_launch_status();
 }
 
@@ -849,7 +910,7 @@ int launch_nl_batch(const double* pos, const BatchPlan& p, double rcut, int32_t 
     A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
     A.status = status;
     const size_t lds = kNlWaves * sizeof(WaveList) + 3 * sizeof(int) * (size_t)p.max_stencil;
-    hipLaunchKernelGGL(select_kernel<true>, dim3((unsigned)p.n_cells, (unsigned)A.nsplit),
+    hipLaunchKernelGGL((select_kernel<true, false>), dim3((unsigned)p.n_cells, (unsigned)A.nsplit),
                        dim3(kNlBlock), (unsigned)lds, s, A);
     return last_launch_status();
 }
