@@ -747,6 +747,15 @@ size_t select_lds_bytes(const Geom& g) {
     return kNlWaves * sizeof(WaveList) + 3 * sizeof(int) * (size_t)g.stencil;
 }
 
+// Candidate rounds that cross segment ends pay off when segments are shorter than about a
+// round and a half: a segment is about one x-row of stencil cells (a single cell when the box
+// has one cell per row, whose images then come as separate segments).
+bool short_segments(int64_t n, const Geom& g) {
+    const double seg_est = (double)n / (double)g.ncells *
+                           (double)std::min(g.nc[0], 2 * g.reach[0] + 1);
+    return seg_est <= 96.0;
+}
+
 int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t sel,
               int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, hipStream_t s) {
     WsLayout w = carve(ws, n, g);
@@ -784,12 +793,7 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     A.table = nullptr;
     A.cell_ptr = nullptr;
     A.n_structs = 1;
-    // Candidate rounds that cross segment ends pay off when segments are shorter than about a
-    // round and a half: a segment is about one x-row of stencil cells (a single cell when the
-    // box has one cell per row, whose images then come as separate segments).
-    const double seg_est = (double)n / (double)g.ncells *
-                           (double)std::min(g.nc[0], 2 * g.reach[0] + 1);
-    const bool flat = seg_est <= 96.0;
+    const bool flat = short_segments(n, g);
     if (flat)
         hipLaunchKernelGGL((select_kernel<false, true>), dim3((unsigned)g.ncells,
                            (unsigned)A.nsplit), dim3(kNlBlock), (unsigned)select_lds_bytes(g), s, A);
@@ -812,6 +816,7 @@ struct BatchPlan {
     int64_t n_cells = 0;
     int max_stencil = 1;
     int nsplit = 1;
+    bool flat = true;  // every structure has short segments
 };
 
 bool plan_batch(int32_t n_structs, const int64_t* atom_ptr, const double* boxes, double rcut,
@@ -833,6 +838,7 @@ bool plan_batch(int32_t n_structs, const int64_t* atom_ptr, const double* boxes,
         p->cell_ptr[b + 1] = p->cell_ptr[b] + g.ncells;
         p->max_stencil = std::max(p->max_stencil, g.stencil);
         max_per_cell = std::max(max_per_cell, (double)nb / (double)g.ncells);
+        p->flat = p->flat && short_segments(nb, g);
     }
     p->n_atoms = atom_ptr[n_structs];
     p->n_cells = p->cell_ptr[n_structs];
@@ -910,8 +916,12 @@ int launch_nl_batch(const double* pos, const BatchPlan& p, double rcut, int32_t 
     A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
     A.status = status;
     const size_t lds = kNlWaves * sizeof(WaveList) + 3 * sizeof(int) * (size_t)p.max_stencil;
-    hipLaunchKernelGGL((select_kernel<true, false>), dim3((unsigned)p.n_cells, (unsigned)A.nsplit),
-                       dim3(kNlBlock), (unsigned)lds, s, A);
+    if (p.flat)
+        hipLaunchKernelGGL((select_kernel<true, true>), dim3((unsigned)p.n_cells,
+                           (unsigned)A.nsplit), dim3(kNlBlock), (unsigned)lds, s, A);
+    else
+        hipLaunchKernelGGL((select_kernel<true, false>), dim3((unsigned)p.n_cells,
+                           (unsigned)A.nsplit), dim3(kNlBlock), (unsigned)lds, s, A);
     return last_launch_status();
 }
 
