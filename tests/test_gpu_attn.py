@@ -105,6 +105,9 @@ CASES = [
     (np.float64, 30, 50, 16, 1, 3, 20),      # fused fp64, one head of 16
     (np.float64, 20, 64, 8, 1, 2, 21),       # fused fp64, one head of 8
     (np.float64, 20, 65, 32, 4, 2, 22),      # rows past 64: fp64 matrix-core path
+    (np.float64, 25, 64, 16, 2, 2, 25),      # fused fp64, two heads of 8 (stacked Q/K tiles)
+    (np.float64, 25, 48, 32, 2, 3, 26),      # fused fp64, two heads of 16, three key tiles
+    (np.float64, 25, 100, 64, 2, 2, 27),     # fp64 matrix-core path, heads of 32, rows < 128
     (np.float32, 20, 192, 64, 4, 2, 23),     # fused fp32 at its 192-row cap (12 full tiles)
     (np.float32, 20, 192, 16, 1, 1, 24),     # the same with one head
 ]
