@@ -117,6 +117,10 @@ def test_ideal_lattices_bitexact(oracle_mod, lattice, ncells, a, rcut, sel):
     (2, (2.0, 9.0, 2.0), 3.0, 50, 5),
     (1000, (30.0, 30.0, 30.0), 2.0, 8, 6),    # sparse: many empty cells
     (700, (40.0, 10.0, 10.0), 2.6, 32, 7),
+    (8192, (60.0, 60.0, 60.0), 3.7, 24, 8),   # one-work-group binning at its limits (4,096 cells)
+    (8193, (60.0, 60.0, 60.0), 3.7, 24, 9),   # one atom past them: multi-launch binning
+    (3000, (20.0, 20.0, 20.0), 5.0, 60, 10),  # ~47 atoms per cell: per-segment candidate rounds
+    (1500, (20.0, 20.0, 20.0), 5.0, 60, 11),  # ~23 atoms per cell: rounds across segment ends
 ])
 def test_random_boxes_bitexact(oracle_mod, n, box, rcut, sel, seed):
     pos = W.random_positions(n, box, seed)
