@@ -12,13 +12,16 @@
 //   2. bin: validate each position, cell id, atomic slot within the cell
 //   3. exclusive scan of cell counts -> cell offsets (scan.hip)
 //   4. scatter atoms into cell order (positions copied bit for bit)
+//      (steps 1-4 are one single-work-group launch for up to 8,192 atoms and 4,096 cells)
 //   5. select: one work-group per (cell, split) with the cell's stencil merged into segments
 //      in LDS; each wavefront takes one centre at a time (about four per work-group and
 //      wavefront), reads the segments' cell-sorted positions with coalesced loads, evaluates
 //      the fp64 distance of every candidate, compacts the accepted ones with ballot/mbcnt into
 //      a per-wave LDS list, sorts them in registers (bitonic on 32-bit words: a distance
 //      class of r2 above the list index, then runs of equal classes re-ranked by the full key
-//      (r2, j, shift)) and writes the first min(sel, count) as the row.
+//      (r2, j, shift)) and writes the first min(sel, count) as the row.  Candidates are
+//      read in rounds of three 64-wide chunks, per segment, or across segment ends when the
+//      segments are short (small boxes, sparse cells).
 //
 // The distance is d = (x_j - x_i) + n*L per axis, r2 = (dx*dx + dy*dy) + dz*dz, in IEEE
 // fp64 with contraction disabled in this file, so every accepted r2 is bit-identical to a
