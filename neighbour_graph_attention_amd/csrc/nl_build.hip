@@ -95,12 +95,21 @@ struct WsLayout {
     int64_t* cell_start;
     int32_t* atom_cell;
     int32_t* atom_slot;
-    double* sx;
-    double* sy;
-    double* sz;
-    int32_t* sidx;
+    // Cell-sorted atoms, 32 bytes each: x, y, z and the atom index (its integer bits in the
+    // fourth double), so that a candidate is two 16-byte loads.
+    double* sa;
     size_t bytes;
 };
+
+typedef double d2 __attribute__((ext_vector_type(2)));
+
+// Atom i at sorted slot d of the cell-sorted array.
+__device__ inline void store_sorted(double* __restrict__ sa, int64_t d, const double* pos,
+                                    int64_t i) {
+    d2* o = reinterpret_cast<d2*>(sa) + 2 * d;
+    o[0] = d2{pos[3 * i + 0], pos[3 * i + 1]};
+    o[1] = d2{pos[3 * i + 2], __longlong_as_double((long long)i)};
+}
 
 WsLayout carve(void* ws, int64_t n, const Geom& g) {
     Carver cv(ws);
@@ -110,10 +119,7 @@ WsLayout carve(void* ws, int64_t n, const Geom& g) {
     w.cell_start = cv.take<int64_t>(g.ncells + 1);
     w.atom_cell = cv.take<int32_t>(n);
     w.atom_slot = cv.take<int32_t>(n);
-    w.sx = cv.take<double>(n);
-    w.sy = cv.take<double>(n);
-    w.sz = cv.take<double>(n);
-    w.sidx = cv.take<int32_t>(n);
+    w.sa = cv.take<double>(4 * n);
     w.bytes = cv.off;
     return w;
 }
@@ -190,15 +196,10 @@ bin_batch_kernel(const double* __restrict__ pos, int n, const BatchGeom* __restr
 __global__ void __launch_bounds__(256)
 scatter_kernel(const double* __restrict__ pos, int n, const int64_t* __restrict__ cell_start,
                const int32_t* __restrict__ atom_cell, const int32_t* __restrict__ atom_slot,
-               double* __restrict__ sx, double* __restrict__ sy, double* __restrict__ sz,
-               int32_t* __restrict__ sidx) {
+               double* __restrict__ sa) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
-    int64_t d = cell_start[atom_cell[i]] + atom_slot[i];
-    sx[d] = pos[3 * (int64_t)i + 0];
-    sy[d] = pos[3 * (int64_t)i + 1];
-    sz[d] = pos[3 * (int64_t)i + 2];
-    sidx[d] = i;
+    store_sorted(sa, cell_start[atom_cell[i]] + atom_slot[i], pos, i);
 }
 
 // Small systems: counting, the exclusive scan of the cell counts and the scatter in one
@@ -213,8 +214,7 @@ constexpr int kSmallCells = 4096;
 
 __global__ void __launch_bounds__(kSmallThreads)
 bin_small_kernel(const double* __restrict__ pos, int n, Geom g, int64_t* __restrict__ cell_start,
-                 double* __restrict__ sx, double* __restrict__ sy, double* __restrict__ sz,
-                 int32_t* __restrict__ sidx, uint32_t* status) {
+                 double* __restrict__ sa, uint32_t* status) {
     __shared__ int32_t s_count[kSmallCells];
     __shared__ int32_t s_wave[kSmallThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -279,13 +279,7 @@ bin_small_kernel(const double* __restrict__ pos, int n, Geom g, int64_t* __restr
 #pragma unroll
     for (int k = 0; k < kSmallPer; ++k) {
         const int i = tid + kSmallThreads * k;
-        if (i < n) {
-            const int d = s_count[cell[k]] + slot[k];
-            sx[d] = pos[3 * (int64_t)i + 0];
-            sy[d] = pos[3 * (int64_t)i + 1];
-            sz[d] = pos[3 * (int64_t)i + 2];
-            sidx[d] = i;
-        }
+        if (i < n) store_sorted(sa, s_count[cell[k]] + slot[k], pos, i);
     }
 }
 
@@ -308,10 +302,7 @@ struct SelectArgs {
     int sel;
     int nsplit;
     const int64_t* cell_start;
-    const double* sx;
-    const double* sy;
-    const double* sz;
-    const int32_t* sidx;
+    const double* sa;  // cell-sorted atoms (WsLayout::sa)
     int32_t* nbr;
     int32_t* nbr_shift;
     int32_t* nnei;
@@ -615,15 +606,13 @@ select_kernel(SelectArgs A) {
     const double Lx = g.L[0], Ly = g.L[1], Lz = g.L[2];
     const double rc2 = A.rc2;
     const int sel = A.sel;
-    const double* __restrict__ sx = A.sx;
-    const double* __restrict__ sy = A.sy;
-    const double* __restrict__ sz = A.sz;
-    const int32_t* __restrict__ sidx = A.sidx;
+    const d2* __restrict__ sa2 = reinterpret_cast<const d2*>(A.sa);
 
     for (int li = blockIdx.y * kNlWaves + wave; li < c1 - c0; li += kNlWaves * A.nsplit) {
         const int ci = c0 + li;
-        const int i = sidx[ci];
-        const double xi = sx[ci], yi = sy[ci], zi = sz[ci];
+        const d2 ci0 = sa2[2 * ci], ci1 = sa2[2 * ci + 1];
+        const int i = (int)__double_as_longlong(ci1[1]);
+        const double xi = ci0[0], yi = ci0[1], zi = ci1[0];
         int count = 0;
         if constexpr (FLAT) {
             // Short segments (small boxes, where most of the stencil is periodic images, or few
@@ -642,10 +631,11 @@ select_kernel(SelectArgs A) {
                         cl[u] = len - off < 64 ? len - off : 64;
                         cc[u] = s_code[sc];
                         const int a = s_start[sc] + off + (lane < cl[u] ? lane : 0);
-                        cx[u] = sx[a];
-                        cy[u] = sy[a];
-                        cz[u] = sz[a];
-                        cj[u] = sidx[a];
+                        const d2 v0 = sa2[2 * a], v1 = sa2[2 * a + 1];
+                        cx[u] = v0[0];
+                        cy[u] = v0[1];
+                        cz[u] = v1[0];
+                        cj[u] = (int)__double_as_longlong(v1[1]);
                         off += 64;
                         if (off >= len) {
                             ++sc;
@@ -690,10 +680,11 @@ select_kernel(SelectArgs A) {
                 for (int u = 0; u < 3; ++u) {
                     const int t = t0 + 64 * u + lane;
                     const int a = base + (t < len ? t : 0);
-                    cx[u] = sx[a];
-                    cy[u] = sy[a];
-                    cz[u] = sz[a];
-                    cj[u] = sidx[a];
+                    const d2 v0 = sa2[2 * a], v1 = sa2[2 * a + 1];
+                    cx[u] = v0[0];
+                    cy[u] = v0[1];
+                    cz[u] = v1[0];
+                    cj[u] = (int)__double_as_longlong(v1[1]);
                 }
 #pragma unroll
                 for (int u = 0; u < 3; ++u) {
@@ -767,7 +758,7 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     int rc;
     if (n <= kSmallAtoms && g.ncells <= kSmallCells) {
         hipLaunchKernelGGL(bin_small_kernel, dim3(1), dim3(kSmallThreads), 0, s, pos, ni, g,
-                           w.cell_start, w.sx, w.sy, w.sz, w.sidx, status);
+                           w.cell_start, w.sa, status);
         if ((rc = last_launch_status())) return rc;
     } else {
         hipLaunchKernelGGL(clear_i32_kernel, dim3((unsigned)((g.ncells + 255) / 256)), dim3(256),
@@ -779,7 +770,7 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
         if ((rc = scan_counts_finish(w.cell_count, g.ncells, w.tile_sums, w.cell_start, s)))
             return rc;
         hipLaunchKernelGGL(scatter_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,
-                           w.cell_start, w.atom_cell, w.atom_slot, w.sx, w.sy, w.sz, w.sidx);
+                           w.cell_start, w.atom_cell, w.atom_slot, w.sa);
         if ((rc = last_launch_status())) return rc;
     }
 
@@ -790,7 +781,7 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     A.sel = sel;
     A.nsplit = select_splits((double)n / (double)g.ncells, g.ncells);
     A.cell_start = w.cell_start;
-    A.sx = w.sx; A.sy = w.sy; A.sz = w.sz; A.sidx = w.sidx;
+    A.sa = w.sa;
     A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
     A.status = status;
     A.table = nullptr;
@@ -903,7 +894,7 @@ int launch_nl_batch(const double* pos, const BatchPlan& p, double rcut, int32_t 
         return rc;
     if (ni == 0) return NGA_OK;
     hipLaunchKernelGGL(scatter_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,
-                       w.cell_start, w.atom_cell, w.atom_slot, w.sx, w.sy, w.sz, w.sidx);
+                       w.cell_start, w.atom_cell, w.atom_slot, w.sa);
     if ((rc = last_launch_status())) return rc;
     SelectArgs A;
     A.g = p.table[0].g;
@@ -915,7 +906,7 @@ int launch_nl_batch(const double* pos, const BatchPlan& p, double rcut, int32_t 
     A.sel = sel;
     A.nsplit = p.nsplit;
     A.cell_start = w.cell_start;
-    A.sx = w.sx; A.sy = w.sy; A.sz = w.sz; A.sidx = w.sidx;
+    A.sa = w.sa;
     A.nbr = nbr; A.nbr_shift = nbr_shift; A.nnei = nnei;
     A.status = status;
     const size_t lds = kNlWaves * sizeof(WaveList) + 3 * sizeof(int) * (size_t)p.max_stencil;
