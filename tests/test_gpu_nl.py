@@ -23,6 +23,9 @@ def _gpu_csr(pos_np, box, rcut, sel, want_vec=True):
     nbr, nbr_shift, nnei = nga.nl_build(pos, box, rcut, sel)
     csr = nga.edge_csr(nbr, nbr_shift, nnei, pos=pos, box=box, want_edge_vec=want_vec)
     nga.check_status(csr["ws"], "csr")
+    plain = nga.edge_csr(nbr, nbr_shift, nnei)  # without edge vectors: same rows
+    for k in ("row_ptr", "col", "shift", "dst"):
+        assert torch.equal(plain[k], csr[k]), k
     out = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in csr.items()
            if k != "ws"}
     out["nbr"] = nbr.cpu().numpy()
