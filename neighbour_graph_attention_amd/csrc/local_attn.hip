@@ -200,7 +200,11 @@ __global__ void __launch_bounds__(kLocalThreads) local_stream_kernel(LocalArgs<T
                 sX[(idx / cv) * sxv + idx % cv] = fetch(j0, rows, idx);
         }
         __syncthreads();
-        // scores: pair p = h * 64 + j, one head per wavefront; R_h reads are broadcasts
+        // scores: pair p = h * 64 + j, one head per wavefront; R_h reads are broadcasts.  With
+        // at most one head per wavefront, lane j of wavefront h keeps its own score for the
+        // softmax step below, and the barrier between the two steps is not needed.
+        const bool own = H <= kLocalThreads / 64;
+        T s_own = T(-INFINITY);
         for (int p = tid; p < H * kLocalChunk; p += kLocalThreads) {
             const int h = p / kLocalChunk, j = p - h * kLocalChunk;
             T s = T(-INFINITY);
@@ -211,12 +215,15 @@ __global__ void __launch_bounds__(kLocalThreads) local_stream_kernel(LocalArgs<T
 #pragma unroll
                 for (int e = 1; e < EV; ++e) s += acc[e];
             }
-            sS[h * (kLocalChunk + 1) + j] = s;
+            if (own)
+                s_own = s;
+            else
+                sS[h * (kLocalChunk + 1) + j] = s;
         }
-        __syncthreads();
+        if (!own) __syncthreads();
         // online softmax: wavefront w owns heads w, w+4, ...
         for (int h = wave; h < H; h += kLocalThreads / 64) {
-            const T s = sS[h * (kLocalChunk + 1) + lane];
+            const T s = own ? s_own : sS[h * (kLocalChunk + 1) + lane];
             T m = s;
             for (int off = 32; off > 0; off >>= 1) {
                 const T o = __shfl_xor(m, off, 64);
