@@ -32,7 +32,7 @@ _lib = None
 
 def build(verbose: bool = False) -> str:
     """Compile oracle.c into liboracle.so (gcc, OpenMP, no FP contraction)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+    cmd = ["gcc", "-O3", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
            "-fPIC", "-shared", _SRC, "-o", _LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))

@@ -30,7 +30,7 @@
  *     centre including itself, and there are no biases, residuals or norms;
  *     stacked layers compose, x <- y.
  *
- * Build: gcc -O2 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
+ * Build: gcc -O3 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC.
  */
 #include <math.h>
 #include <stdint.h>
@@ -96,17 +96,25 @@ int64_t orc_nl_row(const double* pos, int64_t n_atoms, const double* box, double
     orc_cand* cand = (orc_cand*)malloc(cap * sizeof(orc_cand));
     if (!cand) return -1;
 
+    /* An image whose component |d_a| along one axis is already >= rcut is
+     * skipped before the other axes are tried: d_a*d_a then rounds to at
+     * least rcut*rcut (rounding is monotonic) and adding the other,
+     * non-negative squares cannot bring r2 back below it, so the full test
+     * would reject it too.  The kept set is exactly that of the full test. */
     const double* xi = pos + 3 * i;
     for (int64_t j = 0; j < n_atoms; ++j) {
         const double* xj = pos + 3 * j;
-        for (int nx = -K[0]; nx <= K[0]; ++nx)
-            for (int ny = -K[1]; ny <= K[1]; ++ny)
+        for (int nx = -K[0]; nx <= K[0]; ++nx) {
+            const double dx = (xj[0] - xi[0]) + (double)nx * box[0];
+            if (fabs(dx) >= rcut) continue;
+            for (int ny = -K[1]; ny <= K[1]; ++ny) {
+                const double dy = (xj[1] - xi[1]) + (double)ny * box[1];
+                if (fabs(dy) >= rcut) continue;
                 for (int nz = -K[2]; nz <= K[2]; ++nz) {
                     if (j == i && nx == 0 && ny == 0 && nz == 0) continue;
+                    const double dz = (xj[2] - xi[2]) + (double)nz * box[2];
                     const int nn[3] = {nx, ny, nz};
-                    double d[3];
-                    for (int a = 0; a < 3; ++a)
-                        d[a] = (xj[a] - xi[a]) + (double)nn[a] * box[a];
+                    const double d[3] = {dx, dy, dz};
                     double sxy = d[0] * d[0] + d[1] * d[1];
                     double r2 = sxy + d[2] * d[2];
                     if (!(r2 < rc2)) continue;
@@ -121,6 +129,8 @@ int64_t orc_nl_row(const double* pos, int64_t n_atoms, const double* box, double
                     c->j = (int32_t)j;
                     for (int a = 0; a < 3; ++a) { c->n[a] = nn[a]; c->d[a] = d[a]; }
                 }
+            }
+        }
     }
     qsort(cand, cnt, sizeof(orc_cand), orc_cand_cmp);
     int64_t keep = (int64_t)cnt < (int64_t)sel ? (int64_t)cnt : (int64_t)sel;
@@ -211,15 +221,21 @@ int64_t orc_nl_full(const double* pos, int64_t n_atoms, const double* box, doubl
 /* Attention: naive loops, one centre at a time.                             */
 /* ------------------------------------------------------------------------ */
 
-/* y[n][c] = x[n][c] . W[c][c]  (y = x W, W row-major [c_in][c_out]). */
+/* y[n][c] = x[n][c] . W[c][c]  (y = x W, W row-major [c_in][c_out]).
+ * Each y[a][u] starts at 0 and adds x[a][t] * W[t][u] for t = 0, 1, ...,
+ * c-1 in that order; the loop over u is innermost only so that W's rows are
+ * read contiguously. */
 static void orc_matmul(const double* x, int64_t n, int32_t c, const double* W, double* y)
 {
-    for (int64_t a = 0; a < n; ++a)
-        for (int32_t u = 0; u < c; ++u) {
-            double s = 0.0;
-            for (int32_t t = 0; t < c; ++t) s += x[a * c + t] * W[(int64_t)t * c + u];
-            y[a * c + u] = s;
+    for (int64_t a = 0; a < n; ++a) {
+        double* ya = y + a * c;
+        for (int32_t u = 0; u < c; ++u) ya[u] = 0.0;
+        for (int32_t t = 0; t < c; ++t) {
+            const double xt = x[a * c + t];
+            const double* Wt = W + (int64_t)t * c;
+            for (int32_t u = 0; u < c; ++u) ya[u] += xt * Wt[u];
         }
+    }
 }
 
 /*
@@ -235,7 +251,7 @@ static void orc_matmul(const double* x, int64_t n, int32_t c, const double* W, d
  *     o_a[h cols] = (sum_b p_b v_b[h cols]) / Z
  *   Y = o Wo
  * W points at the layer's [4][c][c] weights (q, k, v, o).  scratch holds
- * 4*n*c + n doubles.
+ * 5*n*c + n doubles.
  *
  * Smooth attention ([P2] "Graph-native alternatives": the occupancy-modified
  * weights are w_j = softmax_j * (sum_j e_j / D~), a per-segment scalar
@@ -257,17 +273,26 @@ static void orc_layer_block(const double* X, int64_t n, int32_t c, int32_t heads
     double* v = k + n * c;
     double* o = v + n * c;
     double* s = o + n * c;
+    double* kt = s + n;  /* head h's keys transposed: kt[t][b] = k[b][h*d + t] */
     orc_matmul(X, n, c, W + 0 * cc, q);
     orc_matmul(X, n, c, W + 1 * cc, k);
     orc_matmul(X, n, c, W + 2 * cc, v);
     for (int32_t h = 0; h < heads; ++h) {
         const int32_t c0 = h * d;
+        for (int64_t b = 0; b < n; ++b)
+            for (int32_t t = 0; t < d; ++t) kt[t * n + b] = k[b * c + c0 + t];
         for (int64_t a = 0; a < n; ++a) {
+            /* s_b = (sum over t = 0, 1, ..., d-1 of q_a[t] k_b[t]) * scale, each
+             * sum accumulated in t order; b innermost reads kt's rows contiguously. */
+            for (int64_t b = 0; b < n; ++b) s[b] = 0.0;
+            for (int32_t t = 0; t < d; ++t) {
+                const double qt = q[a * c + c0 + t];
+                const double* kr = kt + (int64_t)t * n;
+                for (int64_t b = 0; b < n; ++b) s[b] += qt * kr[b];
+            }
             double m = -INFINITY;
             for (int64_t b = 0; b < n; ++b) {
-                double dot = 0.0;
-                for (int32_t t = 0; t < d; ++t) dot += q[a * c + c0 + t] * k[b * c + c0 + t];
-                s[b] = dot * scale;
+                s[b] = s[b] * scale;
                 if (s[b] > m) m = s[b];
             }
             double z = 0.0;
@@ -276,11 +301,13 @@ static void orc_layer_block(const double* X, int64_t n, int32_t c, int32_t heads
                 z += s[b];
             }
             const double factor = log_dt ? exp(m + log(z) - log_dt[a * heads + h]) : 1.0;
-            for (int32_t t = 0; t < d; ++t) {
-                double acc = 0.0;
-                for (int64_t b = 0; b < n; ++b) acc += s[b] * v[b * c + c0 + t];
-                o[a * c + c0 + t] = acc / z * factor;
-            }
+            /* o_a[t] = (sum over b = 0, 1, ..., n-1 of p_b v_b[t]) / Z, each sum
+             * accumulated in b order; t innermost reads v's rows contiguously. */
+            double* oa = o + a * c + c0;
+            for (int32_t t = 0; t < d; ++t) oa[t] = 0.0;
+            for (int64_t b = 0; b < n; ++b)
+                for (int32_t t = 0; t < d; ++t) oa[t] += s[b] * v[b * c + c0 + t];
+            for (int32_t t = 0; t < d; ++t) oa[t] = oa[t] / z * factor;
         }
     }
     orc_matmul(o, n, c, W + 3 * cc, Y);
@@ -327,7 +354,7 @@ static int orc_attn_layers(const int64_t* row_ptr, const int32_t* order, int64_t
         {
             double* Xb = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
             double* Yb = (double*)malloc((size_t)(nmax + 1) * c * sizeof(double));
-            double* sc = (double*)malloc(((size_t)4 * (nmax + 1) * c + nmax + 1) * sizeof(double));
+            double* sc = (double*)malloc(((size_t)5 * (nmax + 1) * c + nmax + 1) * sizeof(double));
             double* Lb = (double*)malloc((size_t)(nmax + 1) * heads * sizeof(double));
             if (!Xb || !Yb || !sc || !Lb) failed = 1;
 #pragma omp for schedule(dynamic, 8)
@@ -399,7 +426,7 @@ int orc_attn_naive_centres(const int64_t* row_ptr, const int32_t* order,
                 free(Xb); free(Yb); free(sc);
                 Xb = (double*)malloc((size_t)n * c * sizeof(double));
                 Yb = (double*)malloc((size_t)n * c * sizeof(double));
-                sc = (double*)malloc(((size_t)4 * n * c + n) * sizeof(double));
+                sc = (double*)malloc(((size_t)5 * n * c + n) * sizeof(double));
                 have = n;
                 if (!Xb || !Yb || !sc) { failed = 1; have = -1; continue; }
             }

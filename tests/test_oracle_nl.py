@@ -187,10 +187,11 @@ def test_ideal_diamond_tie_break_by_index(oracle_mod):
         shell9 = [(int(c_full[k]), tuple(s_full[k])) for k in range(nw) if 5.2 < r[k] < 5.4]
         assert len(shell9) == 24
         kept9 = [(int(c[k]), tuple(s[k])) for k in range(98, 120)]
-        # ties broken by index: if the shell shares one r2, the kept 22 are the 22 smallest (j, n)
-        if len(set(r2_full[98:122].tolist())) == 1:
-            assert kept9 == sorted(shell9)[:22]
-        assert set(kept9) <= set(shell9)
+        # On the ideal lattice the whole 24-site shell has one fp64 r2 (exact tie), so the
+        # order inside it is decided by the index alone: the kept 22 are the 22 smallest (j, n).
+        assert len(set(r2_full[98:122].tolist())) == 1
+        assert set(r2[98:120].tolist()) == set(r2_full[98:122].tolist())
+        assert kept9 == sorted(shell9)[:22]
 
 
 @pytest.mark.parametrize("key", [1, 3])
@@ -234,3 +235,38 @@ def test_relabelling_equivariance(oracle_mod):
         assert np.array_equal(perm[c1[a]], c2[b])
         assert np.array_equal(s1[a], s2[b])
         assert np.array_equal(v1[a], v2[b])
+
+
+@pytest.mark.parametrize("case", ["diamond-64", "diamond-1000", "tiny-box"])
+def test_nl_rows_equal_rows_of_nl_full(oracle_mod, case):
+    """nl_rows over a list of centres gives, bit for bit, those centres' rows of nl_full,
+    concatenated in list order (the first and last centre included, duplicates and an
+    unsorted list allowed), with the row lengths as its row_ptr."""
+    if case == "tiny-box":
+        # 30 atoms in a box smaller than rcut on every axis: several images of every atom
+        rng = np.random.default_rng(31)
+        box = (2.5, 3.0, 3.5)
+        pos = rng.uniform(0.0, 1.0, (30, 3)) * np.asarray(box)
+        rcut, sel = 4.0, 150
+    else:
+        w = W.WORKLOADS[1 if case == "diamond-64" else 3]
+        pos, box = W.workload_positions(w)
+        rcut, sel = w.rcut, w.sel
+    n = pos.shape[0]
+    rp, col, shift, vec = oracle_mod.nl_full(pos, box, rcut, sel)
+    rng = np.random.default_rng(32)
+    centres = np.concatenate([[n - 1, 0], rng.choice(n, min(n, 25), replace=False), [0]])
+    srp, scol, sshift, svec = oracle_mod.nl_rows(pos, box, rcut, sel, centres)
+    assert srp.shape == (len(centres) + 1,) and srp[0] == 0
+    for t, i in enumerate(centres):
+        a, b = slice(srp[t], srp[t + 1]), slice(rp[i], rp[i + 1])
+        assert srp[t + 1] - srp[t] == rp[i + 1] - rp[i]
+        assert np.array_equal(scol[a], col[b])
+        assert np.array_equal(sshift[a], shift[b])
+        assert np.array_equal(svec[a], vec[b])
+    assert srp[-1] == len(scol) == len(sshift) == len(svec)
+    if case == "tiny-box":
+        assert np.any(np.abs(shift) >= 2)  # images beyond the neighbouring cells occur
+    # an empty list gives an empty CSR
+    erp, ecol, eshift, evec = oracle_mod.nl_rows(pos, box, rcut, sel, np.zeros(0, np.int64))
+    assert erp.tolist() == [0] and len(ecol) == len(eshift) == len(evec) == 0
