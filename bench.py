@@ -4,9 +4,16 @@
 One step = nl_build (cell-list neighbour rows) + edge_csr (destination CSR) +
 block_attn_forward (all attention layers), every input resident in HBM, all
 on torch's current stream, no host synchronisation inside the step.  The
-workload defaults to Fe BCC, 32^3 cubic cells (65,536 atoms), rcut 8 A,
-sel 181, 64 fp32 channels, 4 heads, 1 layer: the system size at which the
-deepmd-kit DPA4 issue quotes atom-step/s.  Atoms/s = N / step time.
+workload defaults to the largest one: Fe BCC, 37^3 cubic cells with 5% of
+the sites removed (96,241 atoms), rcut 8 A, sel 181, 64 fp32 channels,
+4 heads, 2 layers -- the 101,306-site lattice of the deepmd-kit DPA4 issue's
+largest run.  Atoms/s = N / step time.
+
+Timing follows the DPA4 issue's protocol (warm-up steps, then timed steps;
+20 and 100 by default) with HIP events around every call on the stream the
+library launches on; the median and the 10%-trimmed mean (the mlipaudit
+page's outlier trimming) are reported per call and per step next to the
+wall-clock mean that gives `value`.
 
 Prints one JSON line with the value, a roofline entry for the dominant
 kernel (live HIP-event timing of its launches) and the CPU oracle timed on a
@@ -28,8 +35,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "atoms/s for NL build + block-dense neighbour attention fwd; % of roofline"
 PEAK_TFLOPS = {"f32": 157.3, "f64": 78.6, "f16": 2500.0}   # MI355X dense MFMA peaks
-# The fused fp32 kernel runs every contraction on the f16 matrix cores as (hi, lo) f16
-# pairs: four f16 products per fp32 multiply-add.
+# The f16 split-pair arithmetic (NGA_F32_SPLIT16) runs every contraction on the f16 matrix
+# cores as (hi, lo) f16 pairs: four f16 products per fp32 multiply-add.
 SPLIT_F16_FACTOR = 4.0
 PEAK_HBM_GBS = 8000.0                        # MI355X HBM3E
 
@@ -37,9 +44,12 @@ PEAK_HBM_GBS = 8000.0                        # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=4, help="workload key (1..5), default 4")
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=5, help="workload key (1..5), default 5")
+    ap.add_argument("--split16", action="store_true",
+                    help="also time the NGA_F32_SPLIT16 arithmetic (f16 hi/lo pairs) on the same "
+                         "inputs and report its time and its difference from the fp32 output")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -82,7 +92,9 @@ def source_digest(paths) -> str:
 
 def attention_sources(variant: str):
     base = "neighbour_graph_attention_amd/csrc/"
-    if variant.startswith("fused_f32"):
+    if variant == "fused_f32":
+        return [base + "block_attn_f32.hip", base + "block_attn_fused.h"]
+    if variant == "fused_f32_split16":
         return [base + "block_attn_fused.hip", base + "block_attn_fused.h"]
     if variant == "fused_f64":
         return [base + "block_attn_f64_fused.hip", base + "block_attn_f64.h"]
@@ -123,8 +135,29 @@ def cpu_baseline(w, pos, box, rp, x, wt, target_s):
     m = int(min(n, max(m0, m0 * target_s / max(t0, 1e-6))))
     t = run(m)
     return {"value": m / t, "unit": "atoms/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{m} random centres of {n}: brute-force rows over all atoms and images, "
                       f"then naive attention through {w.layers} layer(s); {t:.1f} s wall"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def robust(ms) -> dict:
+    """Mean, median and 10%-trimmed mean (10% cut at each end) of per-call times in ms."""
+    a = np.sort(np.asarray(ms, dtype=np.float64))
+    k = int(0.1 * a.size)
+    trimmed = a[k:a.size - k] if a.size - 2 * k > 0 else a
+    return {"mean": float(a.mean()), "median": float(np.median(a)),
+            "trimmed_mean_10": float(trimmed.mean()), "min": float(a[0]), "max": float(a[-1])}
 
 
 def time_pair_axis(nga, torch, dev, stream, row_ptr, x, wt, w, rp, steps, chunk, y_block,
@@ -248,6 +281,12 @@ def main():
     part = np.array([[ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
                       ev[2].elapsed_time(ev[3])] for ev in events])
     nl_ms, csr_ms, attn_ms = (float(v) for v in part.mean(axis=0))
+    # Per step on the GPU clock: from the step's first call to the end of its last.
+    step_gpu = [ev[0].elapsed_time(ev[3]) for ev in events]
+    timing = {"protocol": f"{args.warmup} warm-up steps, then {args.steps} timed steps; HIP "
+                          "events around every call on the library's stream",
+              "step_ms": robust(step_gpu), "nl_build_ms": robust(part[:, 0]),
+              "edge_csr_ms": robust(part[:, 1]), "block_attn_forward_ms": robust(part[:, 2])}
 
     batch_rec = None
     if args.nl_batch > 0:
@@ -399,6 +438,36 @@ def main():
                      "achieved_gbs": loc_bytes / (loc_ms * 1e-3) / 1e9,
                      "frac_hbm": loc_bytes / (loc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
+    split_rec = None
+    if args.split16 and w.dtype == "f32":
+        v16 = nga.attn_variant(nga.NGA_F32_SPLIT16, w.sel, w.c, w.heads)
+        ws16 = nga.Workspace(dev, nga.block_attn_workspace_bytes(nga.NGA_F32_SPLIT16, e, w.sel,
+                                                                 w.c, w.heads, w.layers))
+        y16 = torch.empty_like(x)
+        for _ in range(args.warmup):
+            nga.block_attn_forward(csr_out["row_ptr"], x, wt, w.heads, w.sel, y=y16, ws=ws16,
+                                   split16=True)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            nga.block_attn_forward(csr_out["row_ptr"], x, wt, w.heads, w.sel, y=y16, ws=ws16,
+                                   split16=True)
+            e1.record(stream)
+        torch.cuda.synchronize(dev)
+        nga.check_status(ws16, "block_attn_forward (split16)")
+        ms16 = robust([e0.elapsed_time(e1) for e0, e1 in evs])
+        diff = float((y16.double() - y.double()).abs().max() / y.double().abs().max())
+        fl16 = w.layers * float(np.sum(8.0 * w.c * w.c * np.diff(rp) + 4.0 * w.c * np.diff(rp)
+                                      .astype(np.float64) ** 2))
+        split_rec = {"kernel": v16, "block_attn_forward_ms": ms16,
+                     "vs_fp32_kernel": ms16["mean"] / attn_ms,
+                     "frac_of_split_bound": fl16 / (ms16["mean"] * 1e-3) / 1e12
+                     / (PEAK_TFLOPS["f16"] / SPLIT_F16_FACTOR),
+                     "normwise_diff_vs_fp32_output": diff,
+                     "note": "contractions on f16 hi/lo pairs (21-22 significant bits per "
+                             "operand); not fp32 arithmetic, asked for only by NGA_F32_SPLIT16"}
+
     pair_rec = None
     if args.pair_axis:
         pair_rec = time_pair_axis(nga, torch, dev, stream, csr_out["row_ptr"][: n + 1], x, wt, w,
@@ -416,14 +485,8 @@ def main():
     attn_flops = w.layers * float(np.sum(4.0 * w.c * counts * counts))   # S = QK^T and O = PV
     flops = proj_flops + attn_flops
     achieved = flops / (attn_ms * 1e-3) / 1e12
-    if variant.startswith("fused_f32"):
-        # Matrix-core bound of this kernel: all of its flops as split pairs on the f16 pipe.
-        peak = PEAK_TFLOPS["f16"] / SPLIT_F16_FACTOR
-        peak_basis = (f"every contraction as f16 hi/lo pairs: {SPLIT_F16_FACTOR:g} f16 flops per "
-                      f"fp32 flop at {PEAK_TFLOPS['f16']:g} TFLOP/s")
-    else:
-        peak = PEAK_TFLOPS[w.dtype]
-        peak_basis = f"{w.dtype} dense MFMA"
+    peak = PEAK_TFLOPS[w.dtype]
+    peak_basis = f"{w.dtype} dense MFMA"
     traffic = load_traffic(variant, w.name)
     nl_bytes = 24.0 * n + 8.0 * (n + 1) + 16.0 * e
     nl_gbs = nl_bytes / ((nl_ms + csr_ms) * 1e-3) / 1e9
@@ -453,6 +516,7 @@ def main():
                      "kernel": variant, "flops_per_launch": flops, "launch_ms": attn_ms,
                      "peak_basis": peak_basis},
         "parts_ms": {"nl_build": nl_ms, "edge_csr": csr_ms, "block_attn_forward": attn_ms},
+        "timing": timing,
         "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
                    "frac": nl_gbs / PEAK_HBM_GBS},
         "csr_hbm": {"algorithmic_bytes": csr_bytes, "achieved_gbs": csr_gbs,
@@ -470,6 +534,8 @@ def main():
         rec["local_atten"] = local_rec
     if pair_rec is not None:
         rec["pair_axis"] = pair_rec
+    if split_rec is not None:
+        rec["split16"] = split_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, pos_np, box, rp, x_np, wt_np, args.cpu_seconds)
     else:

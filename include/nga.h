@@ -73,7 +73,19 @@ enum {
     NGA_EINDEX = -8      /* an index in device data is out of range */
 };
 
-enum { NGA_F64 = 0, NGA_F32 = 1 };
+/* Feature dtypes of the attention calls.
+ *   NGA_F64          fp64 features, weights and outputs; fp64 arithmetic.
+ *   NGA_F32          fp32 features, weights and outputs; fp32 arithmetic (the
+ *                    contractions on the fp32 matrix cores, fp32 accumulation).
+ *   NGA_F32_SPLIT16  fp32 features, weights and outputs, softmax and
+ *                    accumulation in fp32, but every contraction operand
+ *                    carried as two f16 parts (hi + lo, 21-22 significant
+ *                    bits after a power-of-two scale) on the f16 matrix
+ *                    cores.  Narrower than fp32: asked for by this code only,
+ *                    and only for 1, 2 or 4 heads of width 16 with rows up to
+ *                    192 (other shapes return NGA_EDTYPE); block_attn_forward
+ *                    and block_attn_forward_smooth only. */
+enum { NGA_F64 = 0, NGA_F32 = 1, NGA_F32_SPLIT16 = 2 };
 
 /* Neighbours within rcut that nl_build can rank for one centre. */
 #define NGA_ROW_CAP 512
@@ -165,10 +177,14 @@ int nl_refine(const double* pos, int64_t n_atoms, const double* h_box, double rc
               int32_t cand_sel, const double* h_cand_box, int32_t* nbr, int32_t* nbr_shift,
               int32_t* nnei, void* ws, size_t ws_bytes, void* stream);
 
-/* The largest displacement |pos_i - pos_ref_i| (minimum image per axis) over
- * the atoms, written to the device double *d_max (set to 0 first; enqueued on
- * `stream`, no host synchronisation): the test for reusing candidate rows,
- * d_max < skin / 2. */
+/* The largest displacement |pos_i - pos_ref_i| over the atoms, as the plain
+ * Euclidean distance (no minimum image), written to the device double *d_max
+ * (set to 0 first; enqueued on `stream`, no host synchronisation): the test
+ * for reusing candidate rows built at pos_ref, d_max < skin / 2.  An atom
+ * re-wrapped into the box since pos_ref therefore reads as a displacement of
+ * about one box length and calls for a rebuild (the candidate rows hold image
+ * shifts of the pos_ref images).  A non-finite distance reads as +inf.
+ * h_box is checked as nl_build checks it; the distance does not use it. */
 int nl_max_displacement(const double* pos, const double* pos_ref, int64_t n_atoms,
                         const double* h_box, double* d_max, void* stream);
 
@@ -239,7 +255,8 @@ size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t nnei_cap, 
  * and the next layer reads y.  Every query attends to every edge of its
  * centre, itself included; there are no biases.
  *
- * dtype      NGA_F64 or NGA_F32; x, y and weights share it.
+ * dtype      NGA_F64, NGA_F32 or NGA_F32_SPLIT16; x, y and weights are
+ *            fp64 for the first, fp32 for the other two.
  * row_ptr    [n_centres+1] int64, row_ptr[0] = 0, non-decreasing.
  * order      [row_ptr[n_centres]] int32 permutation of the edge rows, or
  *            NULL (edges already in destination order, as edge_csr
@@ -399,10 +416,12 @@ int nga_sync_status(void* ws, void* stream);
 const char* nga_strerror(int status);
 
 /* Name of the attention kernel block_attn_forward would launch for these
- * shapes, for reporting; never NULL: "fused_f32_d16" (fp32, 16-wide heads,
- * rows <= 192), "fused_f64" (fp64, c <= 32, heads of 8 or 16, rows <= 64),
- * "mfma_f64" (fp64, heads of 8, 16 or 32, rows <= 128), "generic_f32",
- * "generic_f64", or "unsupported" for an unknown dtype. */
+ * shapes, for reporting; never NULL: "fused_f32" (NGA_F32, 1, 2 or 4 heads
+ * of 16, rows <= 192), "fused_f32_split16" (NGA_F32_SPLIT16, same shapes),
+ * "fused_f64" (fp64, c <= 32, heads of 8 or 16, rows <= 64), "mfma_f64"
+ * (fp64, heads of 8, 16 or 32, rows <= 128), "generic_f32", "generic_f64",
+ * or "unsupported" for an unknown dtype or a shape NGA_F32_SPLIT16 does not
+ * cover. */
 const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads);
 
 #ifdef __cplusplus

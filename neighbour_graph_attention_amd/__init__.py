@@ -15,6 +15,7 @@ built (``neighbour_graph_attention_amd._build.build()``).
 from ._lib import (  # noqa: F401
     EXPORTS,
     NGA_F32,
+    NGA_F32_SPLIT16,
     NGA_F64,
     ROW_CAP,
     NGAError,

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libnga.so")
 
 NGA_OK, NGA_EINVAL, NGA_EBOX, NGA_EROWCAP, NGA_ECAP, NGA_EDTYPE, NGA_EWORKSPACE, NGA_EHIP, \
     NGA_EINDEX = 0, -1, -2, -3, -4, -5, -6, -7, -8
-NGA_F64, NGA_F32 = 0, 1
+NGA_F64, NGA_F32, NGA_F32_SPLIT16 = 0, 1, 2
 ROW_CAP = 512
 
 EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "edge_csr",
@@ -263,11 +263,13 @@ def edge_csr(nbr: torch.Tensor, nbr_shift: torch.Tensor, nnei: torch.Tensor | No
     return res
 
 
-def _attn_dtype(t: torch.Tensor) -> int:
+def _attn_dtype(t: torch.Tensor, split16: bool = False) -> int:
     if t.dtype == torch.float64:
+        if split16:
+            raise TypeError("split16 applies to float32 features only")
         return NGA_F64
     if t.dtype == torch.float32:
-        return NGA_F32
+        return NGA_F32_SPLIT16 if split16 else NGA_F32
     raise TypeError(f"attention features must be float64 or float32, got {t.dtype}")
 
 
@@ -283,14 +285,15 @@ def attn_variant(dtype: int, nnei_cap: int, c: int, n_heads: int) -> str:
 def block_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Tensor,
                        n_heads: int, nnei_cap: int, *, order: torch.Tensor | None = None,
                        y: torch.Tensor | None = None, ws: Workspace | None = None,
-                       log_dtilde: torch.Tensor | None = None):
+                       log_dtilde: torch.Tensor | None = None, split16: bool = False):
     """Stacked block-dense attention layers; returns y [E][c] (same dtype as x).  With
     log_dtilde ([layers][E][n_heads], ln D~ per query edge and head) the smooth form,
-    block_attn_forward_smooth, runs instead."""
+    block_attn_forward_smooth, runs instead.  split16 (float32 only) asks for the
+    NGA_F32_SPLIT16 arithmetic: contractions on f16 hi/lo pairs instead of fp32."""
     lib = load()
     dev = x.device
     e, c = x.shape
-    dt = _attn_dtype(x)
+    dt = _attn_dtype(x, split16)
     n_centres = row_ptr.shape[0] - 1
     _need(row_ptr, "row_ptr", torch.int64, (n_centres + 1,), dev)
     if weights.dim() != 4:
@@ -488,8 +491,9 @@ def nl_refine(pos: torch.Tensor, box, rcut: float, sel: int, cand_nbr: torch.Ten
 
 def nl_max_displacement(pos: torch.Tensor, pos_ref: torch.Tensor, box,
                         out: torch.Tensor | None = None) -> torch.Tensor:
-    """Largest minimum-image displacement between pos and pos_ref, as a 1-element device
-    tensor (no synchronisation)."""
+    """Largest plain (not minimum-image) displacement |pos - pos_ref| over the atoms, as a
+    1-element device tensor (no synchronisation); a re-wrapped atom reads as about one box
+    length."""
     lib = load()
     dev = pos.device
     n = pos.shape[0]

@@ -13,9 +13,9 @@
 //   qkv[s]  = x[order(s)] [Wq | Wk | Wv]           (row-gather GEMM)
 //   o[s]    = per-centre attention of qkv rows      (one work-group per centre)
 //   y[order(s)] = o[s] Wo                           (row-scatter GEMM)
-// The fused fp32 kernel for 16-wide heads lives in block_attn_fused.hip and the fp64
-// matrix-core path for heads of width 8, 16 and 32 in block_attn_f64.hip; this path covers
-// every other shape.
+// The fused fp32 kernel for 16-wide heads lives in block_attn_f32.hip (its f16 split-pair
+// variant, dtype NGA_F32_SPLIT16, in block_attn_fused.hip), the fp64 kernels in
+// block_attn_f64_fused.hip and block_attn_f64.hip; this path covers every other shape.
 #include "nga_internal.h"
 #include "block_attn_f64.h"
 #include "block_attn_fused.h"
@@ -60,12 +60,13 @@ template <typename T, int DMAX>
 __global__ void __launch_bounds__(256) attn_core_kernel(CoreArgs<T> A) {
     const int i = blockIdx.x;
     const int64_t r0 = A.row_ptr[i], r1 = A.row_ptr[i + 1];
-    const int n = (int)(r1 - r0);
-    if (n <= 0) return;
-    if (n > A.nnei_cap || r1 > A.n_edges) {
+    // A decreasing row_ptr, or a row outside [0, n_edges), is reported and the row skipped.
+    if (r0 < 0 || r1 < r0 || r1 > A.n_edges || r1 - r0 > A.nnei_cap) {
         if (threadIdx.x == 0) raise_bits(A.status, kBitCap);
         return;
     }
+    const int n = (int)(r1 - r0);
+    if (n == 0) return;
     const int c = A.c, c3 = 3 * A.c, d = A.d;
     for (int idx = threadIdx.x; idx < n * A.heads; idx += blockDim.x) {
         const int a = idx / A.heads, h = idx % A.heads;
@@ -219,8 +220,17 @@ int run_generic(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
     return NGA_OK;
 }
 
-bool use_fused(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
+// The f16 split-pair arithmetic exists only as the fused kernel for its shapes.
+bool use_split16(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
     return fused_supported(dtype, nnei_cap, c, heads);
+}
+
+bool use_f32_fused(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
+    return dtype == NGA_F32 && f32_fused_supported(nnei_cap, c, heads);
+}
+
+bool known_dtype(int dtype) {
+    return dtype == NGA_F64 || dtype == NGA_F32 || dtype == NGA_F32_SPLIT16;
 }
 
 }  // namespace
@@ -229,11 +239,17 @@ bool use_fused(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
 
 extern "C" size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t nnei_cap,
                                              int32_t c, int32_t n_heads, int32_t n_layers) {
-    if (dtype != NGA_F64 && dtype != NGA_F32) return 0;
+    if (!nga::known_dtype(dtype)) return 0;
     if (n_edges < 0 || c < 1 || n_heads < 1 || n_layers < 1 || nnei_cap < 1) return 0;
-    if (nga::use_fused(dtype, nnei_cap, c, n_heads)) {
+    if (dtype == NGA_F32_SPLIT16) {
+        if (!nga::use_split16(dtype, nnei_cap, c, n_heads)) return 0;
         nga::Carver cv(nullptr);
         cv.take<float>(nga::fused_workspace_floats(c, n_layers));
+        return cv.off;
+    }
+    if (nga::use_f32_fused(dtype, nnei_cap, c, n_heads)) {
+        nga::Carver cv(nullptr);
+        cv.take<float>(nga::f32_fused_workspace_floats(c, n_layers));
         return cv.off;
     }
     if (dtype == NGA_F64 && nga::fused_f64_supported(nnei_cap, c, n_heads))
@@ -243,8 +259,11 @@ extern "C" size_t block_attn_workspace_bytes(int dtype, int64_t n_edges, int32_t
 }
 
 extern "C" const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads) {
-    if (dtype != NGA_F64 && dtype != NGA_F32) return "unsupported";
-    if (nga::use_fused(dtype, nnei_cap, c, n_heads)) return nga::fused_name(dtype, c, n_heads);
+    if (!nga::known_dtype(dtype)) return "unsupported";
+    if (dtype == NGA_F32_SPLIT16)
+        return nga::use_split16(dtype, nnei_cap, c, n_heads) ? nga::fused_name(dtype, c, n_heads)
+                                                             : "unsupported";
+    if (nga::use_f32_fused(dtype, nnei_cap, c, n_heads)) return "fused_f32";
     if (dtype == NGA_F64 && nga::fused_f64_supported(nnei_cap, c, n_heads)) return "fused_f64";
     if (dtype == NGA_F64 && nga::f64_mfma_supported(nnei_cap, c, n_heads)) return "mfma_f64";
     return dtype == NGA_F64 ? "generic_f64" : "generic_f32";
@@ -257,11 +276,13 @@ int attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order, int64_
                  int64_t n_edges, int32_t nnei_cap, int32_t c, int32_t n_heads, int32_t n_layers,
                  const void* weights, const void* x, const void* ldt, void* y, void* ws,
                  size_t ws_bytes, void* stream) {
-    if (dtype != NGA_F64 && dtype != NGA_F32) return NGA_EDTYPE;
+    if (!known_dtype(dtype)) return NGA_EDTYPE;
     if (n_centres < 0 || n_centres >= INT32_MAX || n_edges < 0 || nnei_cap < 1 || c < 1 ||
         n_heads < 1 || c % n_heads != 0 || n_layers < 1)
         return NGA_EINVAL;
     if (c / n_heads > 128) return NGA_EINVAL;
+    // The split-pair arithmetic has no kernel outside its shapes.
+    if (dtype == NGA_F32_SPLIT16 && !use_split16(dtype, nnei_cap, c, n_heads)) return NGA_EDTYPE;
     if (!row_ptr) return NGA_EINVAL;
     if (n_edges > 0 && (!x || !y || !weights)) return NGA_EINVAL;
     const size_t es = dtype == NGA_F64 ? sizeof(double) : sizeof(float);
@@ -276,7 +297,15 @@ int attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order, int64_
     if (n_centres == 0 || n_edges == 0) return NGA_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint32_t* status = &static_cast<WsHeader*>(ws)->status;
-    if (use_fused(dtype, nnei_cap, c, n_heads)) {  // the fused kernel checks row_ptr itself
+    if (use_f32_fused(dtype, nnei_cap, c, n_heads)) {  // the fused kernel checks row_ptr itself
+        Carver cv(ws);
+        float* packed = cv.take<float>(f32_fused_workspace_floats(c, n_layers));
+        return run_f32_fused(row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,
+                             static_cast<const float*>(weights), static_cast<const float*>(x),
+                             static_cast<const float*>(ldt), static_cast<float*>(y), packed,
+                             status, s);
+    }
+    if (dtype == NGA_F32_SPLIT16) {  // the fused kernel checks row_ptr itself
         Carver cv(ws);
         float* packed = cv.take<float>(fused_workspace_floats(c, n_layers));
         return run_fused(dtype, row_ptr, order, n_centres, n_edges, nnei_cap, c, n_heads, n_layers,

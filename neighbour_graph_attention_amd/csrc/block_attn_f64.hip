@@ -278,12 +278,13 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 2) attn_core_f64_kernel(CoreF
         if (A.row_ptr[0] != 0 || A.row_ptr[A.n_centres] > A.n_edges) raise_bits(A.status, kBitCap);
     }
     const int64_t r0 = A.row_ptr[centre], r1 = A.row_ptr[centre + 1];
-    const int n = (int)(r1 - r0);
-    if (n <= 0) return;
-    if (n > A.nnei_cap || n > 16 * kF64TileMax || r0 < 0 || r1 > A.n_edges) {
+    if (r1 == r0) return;
+    if (r1 < r0 || r1 - r0 > A.nnei_cap || r1 - r0 > 16 * kF64TileMax || r0 < 0 ||
+        r1 > A.n_edges) {
         if (threadIdx.x == 0 && h == 0) raise_bits(A.status, kBitCap);
         return;
     }
+    const int n = (int)(r1 - r0);
     const int nt = (n + 15) >> 4;
     const double scale2 = A.scale * kLog2eF64;  // softmax exponents in base 2
     const int c = A.c, c3 = 3 * A.c;

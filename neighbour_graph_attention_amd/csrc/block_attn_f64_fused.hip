@@ -219,12 +219,13 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f64_kernel(FusedF64Args A) {
     const int centre = blockIdx.x;
     const int64_t r0 = A.row_ptr[centre];
     const int64_t r1 = A.row_ptr[centre + 1];
-    const int n = (int)(r1 - r0);
-    if (n <= 0) return;
-    if (n > A.nnei_cap || n > 16 * kFusedF64Tiles || r0 < 0 || r1 > A.n_edges) {
+    if (r1 == r0) return;
+    if (r1 < r0 || r1 - r0 > A.nnei_cap || r1 - r0 > 16 * kFusedF64Tiles || r0 < 0 ||
+        r1 > A.n_edges) {
         if (threadIdx.x == 0) raise_bits(A.status, kBitCap);
         return;
     }
+    const int n = (int)(r1 - r0);
     const int nt = (n + 15) >> 4;
     bool bad_index = false;
     for (int idx = threadIdx.x; idx < 16 * nt * C; idx += 64 * H) {

@@ -1,4 +1,7 @@
-// Fused per-centre block attention, fp32 results, 16-wide heads, on CDNA matrix cores.
+// Fused per-centre block attention, fp32 results, 16-wide heads, on the f16 matrix cores with
+// every contraction operand carried as an f16 (hi, lo) pair.  This is the NGA_F32_SPLIT16
+// arithmetic, asked for by that dtype only: NGA_F32 runs the fp32 matrix-core kernel of
+// block_attn_f32.hip.
 //
 // deepmd-kit issue "perf: NeighborGraph attention is 4-9x slower than dense ...", section
 // "Proposed fix: block-dense attention on the graph": gather a centre's (nnei, c) block
@@ -460,7 +463,7 @@ __device__ inline int split_block(f4 (&vals)[PER], int chunks, unsigned char* sX
 }
 
 template <int H, int TMAX, bool SMOOTH>
-__global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
+__global__ void __launch_bounds__(64 * H, 2) fused_f32_split16_kernel(FusedArgs A) {
     constexpr int C = 16 * H;
     constexpr int U = C / 16;
     constexpr int NTH = 64 * H;
@@ -483,12 +486,14 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_d16_kernel(FusedArgs A) {
         const int centre = blockIdx.x;
         const int64_t r0 = A.row_ptr[centre];
         const int64_t r1 = A.row_ptr[centre + 1];
-        const int n = (int)(r1 - r0);
-        if (n <= 0) return;
-        if (n > A.nnei_cap || n > 16 * TMAX || r0 < 0 || r1 > A.n_edges) {
+        if (r1 == r0) return;
+        // A decreasing row_ptr, a row outside [0, n_edges) or one longer than the cap is
+        // reported and skipped.
+        if (r1 < r0 || r1 - r0 > A.nnei_cap || r1 - r0 > 16 * TMAX || r0 < 0 || r1 > A.n_edges) {
             if (threadIdx.x == 0) raise_bits(A.status, kBitCap);
             return;
         }
+        const int n = (int)(r1 - r0);
         const int nt = (n + 15) >> 4;
         const int chunks = 16 * nt * CH;
         f4 v[PER];
@@ -548,11 +553,11 @@ template <int H, bool SMOOTH>
 int launch_hs(int tmax, const FusedArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_centres), block(64 * H);
     if (tmax <= 4)
-        hipLaunchKernelGGL((fused_f32_d16_kernel<H, 4, SMOOTH>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((fused_f32_split16_kernel<H, 4, SMOOTH>), grid, block, 0, s, a);
     else if (tmax <= 8)
-        hipLaunchKernelGGL((fused_f32_d16_kernel<H, 8, SMOOTH>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((fused_f32_split16_kernel<H, 8, SMOOTH>), grid, block, 0, s, a);
     else
-        hipLaunchKernelGGL((fused_f32_d16_kernel<H, 12, SMOOTH>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((fused_f32_split16_kernel<H, 12, SMOOTH>), grid, block, 0, s, a);
     return last_launch_status();
 }
 
@@ -564,7 +569,7 @@ int launch_h(int tmax, const FusedArgs& a, hipStream_t s) {
 }  // namespace
 
 bool fused_supported(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
-    if (dtype != NGA_F32) return false;
+    if (dtype != NGA_F32_SPLIT16) return false;
     if (heads < 1 || c != 16 * heads) return false;
     if (heads != 1 && heads != 2 && heads != 4) return false;
     return nnei_cap >= 1 && nnei_cap <= 16 * 12;
@@ -572,7 +577,7 @@ bool fused_supported(int dtype, int32_t nnei_cap, int32_t c, int32_t heads) {
 
 const char* fused_name(int dtype, int32_t c, int32_t heads) {
     (void)dtype; (void)c; (void)heads;
-    return "fused_f32_d16";
+    return "fused_f32_split16";
 }
 
 size_t fused_workspace_floats(int32_t c, int32_t layers) { return (size_t)layers * 4 * c * c + 64 + 4 * layers; }

@@ -1030,20 +1030,22 @@ __global__ void __launch_bounds__(kNlBlock) refine_kernel(RefineArgs A) {
 
 __global__ void zero_f64_kernel(double* p) { *p = 0.0; }
 
-// max over atoms of |pos - pos_ref| (minimum image per axis), via an atomic max on the bit
-// patterns (non-negative doubles order as their signed 64-bit patterns).
+// max over atoms of the plain distance |pos - pos_ref| (no minimum image), via an atomic max on
+// the bit patterns (non-negative doubles order as their signed 64-bit patterns).  The cached
+// candidate rows store image shifts taken at pos_ref, so an atom that was re-wrapped into the box
+// since then must read as a displacement of about one box length, which forces a rebuild; a
+// minimum-image distance would hide the wrap and let stale shifts drop its pairs.
 __global__ void __launch_bounds__(256)
 max_displacement_kernel(const double* __restrict__ pos, const double* __restrict__ ref, int n,
-                        double Lx, double Ly, double Lz, double* out) {
+                        double* out) {
     double m = 0.0;
     for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-        double dx = pos[3 * (int64_t)i] - ref[3 * (int64_t)i];
-        double dy = pos[3 * (int64_t)i + 1] - ref[3 * (int64_t)i + 1];
-        double dz = pos[3 * (int64_t)i + 2] - ref[3 * (int64_t)i + 2];
-        dx -= Lx * rint(dx / Lx);
-        dy -= Ly * rint(dy / Ly);
-        dz -= Lz * rint(dz / Lz);
-        const double d = sqrt((dx * dx + dy * dy) + dz * dz);
+        const double dx = pos[3 * (int64_t)i] - ref[3 * (int64_t)i];
+        const double dy = pos[3 * (int64_t)i + 1] - ref[3 * (int64_t)i + 1];
+        const double dz = pos[3 * (int64_t)i + 2] - ref[3 * (int64_t)i + 2];
+        // A NaN distance must not read as "no displacement": it becomes +inf.
+        double d = sqrt((dx * dx + dy * dy) + dz * dz);
+        if (!(d <= 1.79769313486231570e308)) d = INFINITY;
         m = d > m ? d : m;
     }
     for (int off = 32; off > 0; off >>= 1) {
@@ -1126,7 +1128,7 @@ extern "C" int nl_max_displacement(const double* pos, const double* pos_ref, int
         int64_t blocks = (n_atoms + 255) / 256;
         if (blocks > 1024) blocks = 1024;
         hipLaunchKernelGGL(max_displacement_kernel, dim3((unsigned)blocks), dim3(256), 0, s, pos,
-                           pos_ref, (int)n_atoms, h_box[0], h_box[1], h_box[2], d_max);
+                           pos_ref, (int)n_atoms, d_max);
     }
     return last_launch_status();
 }

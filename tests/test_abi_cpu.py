@@ -108,6 +108,10 @@ def test_block_attn_rejects_bad_arguments():
                                       ctypes.c_void_p(x), ctypes.c_void_p(y), ws, wsb, None)
 
     assert call(dt=7) == L.NGA_EDTYPE
+    # split-pair arithmetic outside its shapes: no kernel, so a dtype error before any launch
+    assert call(dt=L.NGA_F32_SPLIT16, c=40, h=5) == L.NGA_EDTYPE
+    assert call(dt=L.NGA_F32_SPLIT16, c=64, h=4, cap=193) == L.NGA_EDTYPE
+    assert call(dt=L.NGA_F32_SPLIT16, c=64, h=4, cap=181, nc=0) == L.NGA_OK
     assert call(c=18, h=4) == L.NGA_EINVAL           # c not divisible by heads
     assert call(h=0) == L.NGA_EINVAL
     assert call(layers=0) == L.NGA_EINVAL
@@ -132,6 +136,7 @@ def test_pair_attn_rejects_bad_arguments():
                                      ctypes.c_void_p(x), ctypes.c_void_p(y), chunk, ws, wsb, None)
 
     assert call(dt=7) == L.NGA_EDTYPE
+    assert call(dt=L.NGA_F32_SPLIT16) == L.NGA_EDTYPE  # block attention only
     assert call(c=18, h=4) == L.NGA_EINVAL           # c not divisible by heads
     assert call(h=0) == L.NGA_EINVAL
     assert call(layers=0) == L.NGA_EINVAL
@@ -163,6 +168,7 @@ def test_local_attn_rejects_bad_arguments():
                                       ctypes.c_void_p(yc), ws, wsb, None)
 
     assert call(dt=7) == L.NGA_EDTYPE
+    assert call(dt=L.NGA_F32_SPLIT16) == L.NGA_EDTYPE  # block attention only
     assert call(c=18, h=4) == L.NGA_EINVAL           # c not divisible by heads
     assert call(c=512, h=4) == L.NGA_EINVAL          # c above 256
     assert call(c=6, h=2) == L.NGA_EINVAL            # c not a multiple of 4
@@ -244,10 +250,20 @@ def test_attention_workspace_and_variant_queries():
     assert nga.attn_variant(L.NGA_F64, 129, 128, 4) == "generic_f64"   # rows past 128
     assert nga.attn_variant(L.NGA_F64, 40, 16, 4) == "generic_f64"     # head width 4
     assert nga.attn_variant(L.NGA_F64, 40, 20, 2) == "generic_f64"     # head width 10
-    assert nga.attn_variant(L.NGA_F32, 181, 64, 4) == "fused_f32_d16"
-    assert nga.attn_variant(L.NGA_F32, 192, 16, 1) == "fused_f32_d16"
+    assert nga.attn_variant(L.NGA_F32, 181, 64, 4) == "fused_f32"      # fp32 matrix cores
+    assert nga.attn_variant(L.NGA_F32, 192, 16, 1) == "fused_f32"
+    assert nga.attn_variant(L.NGA_F32, 96, 32, 2) == "fused_f32"
     assert nga.attn_variant(L.NGA_F32, 193, 64, 4) == "generic_f32"    # rows past 192
     assert nga.attn_variant(L.NGA_F32, 60, 40, 5) == "generic_f32"     # head width 8
+    assert nga.attn_variant(L.NGA_F32, 60, 48, 3) == "generic_f32"     # three heads of 16
+    # the f16 split-pair arithmetic only when asked for, and only for its shapes
+    assert nga.attn_variant(L.NGA_F32_SPLIT16, 181, 64, 4) == "fused_f32_split16"
+    assert nga.attn_variant(L.NGA_F32_SPLIT16, 192, 16, 1) == "fused_f32_split16"
+    assert nga.attn_variant(L.NGA_F32_SPLIT16, 193, 64, 4) == "unsupported"
+    assert nga.attn_variant(L.NGA_F32_SPLIT16, 60, 40, 5) == "unsupported"
+    assert lib.block_attn_workspace_bytes(L.NGA_F32_SPLIT16, 1000, 193, 64, 4, 1) == 0
+    assert lib.block_attn_workspace_bytes(L.NGA_F32_SPLIT16, 1000, 181, 64, 4, 2) > 0
+    assert lib.block_attn_workspace_bytes(L.NGA_F32, 1000, 181, 64, 4, 2) >= 2 * 4 * 64 * 64 * 4
     assert nga.attn_variant(5, 40, 32, 4) == "unsupported"
 
 
@@ -260,9 +276,10 @@ def test_bench_traffic_lookup_names_each_kernels_sources():
 
     import bench
     variants = {nga.attn_variant(dt, cap, c, h) for dt, cap, c, h in [
-        (L.NGA_F32, 181, 64, 4), (L.NGA_F64, 40, 32, 4), (L.NGA_F64, 120, 128, 4),
-        (L.NGA_F64, 40, 20, 2), (L.NGA_F32, 60, 40, 5)]}
-    assert variants == {"fused_f32_d16", "fused_f64", "mfma_f64", "generic_f64", "generic_f32"}
+        (L.NGA_F32, 181, 64, 4), (L.NGA_F32_SPLIT16, 181, 64, 4), (L.NGA_F64, 40, 32, 4),
+        (L.NGA_F64, 120, 128, 4), (L.NGA_F64, 40, 20, 2), (L.NGA_F32, 60, 40, 5)]}
+    assert variants == {"fused_f32", "fused_f32_split16", "fused_f64", "mfma_f64", "generic_f64",
+                        "generic_f32"}
     for v in variants:
         for path in bench.attention_sources(v):
             assert os.path.exists(os.path.join(bench.ROOT, path)), (v, path)

@@ -25,12 +25,12 @@ def _normwise(y, ref):
     return float(np.max(np.abs(y - ref)) / np.max(np.abs(ref)))
 
 
-def _run(row_ptr, x, w, heads, cap, order=None, ws=None):
+def _run(row_ptr, x, w, heads, cap, order=None, ws=None, split16=False):
     ws = ws or nga.Workspace(DEV)
     y = nga.block_attn_forward(torch.from_numpy(row_ptr).to(DEV), torch.from_numpy(x).to(DEV),
                                torch.from_numpy(w).to(DEV), heads, cap,
                                order=None if order is None else torch.from_numpy(order).to(DEV),
-                               ws=ws)
+                               ws=ws, split16=split16)
     nga.check_status(ws, "attention")
     return y.cpu().numpy()
 
@@ -61,24 +61,40 @@ def test_diamond_workloads_whole_output(oracle_mod, key):
 
 
 @pytest.mark.parametrize("key", [4, 5])
-def test_fe_bcc_full_size_sampled_centres(oracle_mod, key):
+def test_fe_bcc_full_size_whole_output(oracle_mod, key):
+    """The Fe BCC workloads at full size, every output row of every centre against the oracle
+    (fp64 naive loops on the same fp32 inputs, through every layer), for the fp32 matrix-core
+    kernel and for the f16 split-pair arithmetic.  A sampled comparison of 200 centres runs
+    first as a quick pre-check."""
     w = W.WORKLOADS[key]
     pos, box, rp, e = _gpu_workload_csr(w)
     n = rp.shape[0] - 1
+    rp_ref, _, _, _ = oracle_mod.nl_full(pos, box, w.rcut, w.sel)
+    assert np.array_equal(rp, rp_ref)
     x = W.workload_features(w, e)
     wt = W.workload_weights(w)
     print(f"workload {w.name} N={n} E={e} variant={nga.attn_variant(1, w.sel, w.c, w.heads)}",
           flush=True)
     y = _run(rp, x, wt, w.heads, w.sel)
+    y16 = _run(rp, x, wt, w.heads, w.sel, split16=True)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(y16))
     rng = np.random.default_rng(2000 + key)
     centres = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 200, replace=False)]))
-    ref = oracle_mod.attn_naive_centres(rp, x.astype(np.float64), wt.astype(np.float64), w.heads,
-                                        centres)
+    x64 = x.astype(np.float64)
+    w64 = wt.astype(np.float64)
+    ref_s = oracle_mod.attn_naive_centres(rp, x64, w64, w.heads, centres)
     rows = np.concatenate([np.arange(rp[i], rp[i + 1]) for i in centres])
-    err = _normwise(y[rows].astype(np.float64), ref[rows])
-    print(f"sampled normwise error {err:.3e}", flush=True)
+    err_s = _normwise(y[rows].astype(np.float64), ref_s[rows])
+    print(f"sampled normwise error {err_s:.3e}", flush=True)
+    assert err_s < TOL[np.float32]
+    del ref_s
+    ref = oracle_mod.attn_naive(rp, x64, w64, w.heads)
+    del x64
+    err = _normwise(y.astype(np.float64), ref)
+    err16 = _normwise(y16.astype(np.float64), ref)
+    print(f"whole-output normwise error: fp32 {err:.3e}, f16 split pairs {err16:.3e}", flush=True)
     assert err < TOL[np.float32]
-    assert np.all(np.isfinite(y))
+    assert err16 < TOL[np.float32]
 
 
 CASES = [
@@ -113,8 +129,19 @@ CASES = [
 ]
 
 
+SPLIT16_CASES = [c for c in CASES if c[0] == np.float32 and c[3] == 16 * c[4] and c[4] in (1, 2, 4)
+                 and c[2] <= 192]
+
+
+@pytest.mark.parametrize("dtype,nc,maxlen,c,heads,layers,seed", SPLIT16_CASES)
+def test_random_ragged_rows_split16(oracle_mod, dtype, nc, maxlen, c, heads, layers, seed):
+    """The f16 split-pair arithmetic (NGA_F32_SPLIT16) on the fp32 cases its kernel covers."""
+    assert nga.attn_variant(nga.NGA_F32_SPLIT16, maxlen, c, heads) == "fused_f32_split16"
+    test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, seed, split16=True)
+
+
 @pytest.mark.parametrize("dtype,nc,maxlen,c,heads,layers,seed", CASES)
-def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, seed):
+def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, seed, split16=False):
     rp = W.random_rows(nc, maxlen, seed)
     # force the edge cases: an empty row, a one-edge row, a full-cap row, tile boundaries
     lens = np.diff(rp)
@@ -125,12 +152,14 @@ def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, see
     e = int(rp[-1])
     x = W.make_features(e, c, seed + 100, dtype)
     wt = W.make_weights(layers, c, seed + 200, dtype)
+    dt = nga.NGA_F64 if dtype == np.float64 else (nga.NGA_F32_SPLIT16 if split16 else nga.NGA_F32)
     print(f"case dtype={dtype.__name__} c={c} H={heads} L={layers} E={e} "
-          f"variant={nga.attn_variant(0 if dtype == np.float64 else 1, maxlen, c, heads)}",
-          flush=True)
-    y = _run(rp, x, wt, heads, maxlen)
+          f"variant={nga.attn_variant(dt, maxlen, c, heads)}", flush=True)
+    y = _run(rp, x, wt, heads, maxlen, split16=split16)
     ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), heads)
-    assert _normwise(y.astype(np.float64), ref) < TOL[dtype]
+    err = _normwise(y.astype(np.float64), ref)
+    print(f"normwise error {err:.3e}", flush=True)
+    assert err < TOL[dtype]
 
 
 def _per_centre_normwise(y, ref, rp):
@@ -141,7 +170,8 @@ def _per_centre_normwise(y, ref, rp):
     return worst
 
 
-def test_f32_split_rounding_ties(oracle_mod):
+@pytest.mark.parametrize("split16", [True, False])
+def test_f32_split_rounding_ties(oracle_mod, split16):
     """fp32 projections on f16 matrix cores take each operand as two f16 parts (hi, lo).  Both
     parts must come from one rounded fp32 value: a head-output element at an f16 rounding tie
     otherwise gets its lo part from a differently rounded copy and lands one f16 ulp off.  The
@@ -154,15 +184,16 @@ def test_f32_split_rounding_ties(oracle_mod):
     lens = np.random.default_rng(31).integers(30, 49, 400)
     rp = np.concatenate([[0, 41], 41 + np.cumsum(lens)]).astype(np.int64)
     x = np.concatenate([blk, W.make_features(int(lens.sum()), 64, 32, np.float32)])
-    y = _run(rp, x, wt, 4, 64)
+    y = _run(rp, x, wt, 4, 64, split16=split16)
     ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), 4)
     err = _per_centre_normwise(y.astype(np.float64), ref, rp)
     print(f"worst per-centre normwise error {err:.3e}", flush=True)
     assert err < TOL[np.float32]
 
 
+@pytest.mark.parametrize("split16", [False, True])
 @pytest.mark.parametrize("heads,layers", [(4, 2), (2, 1), (1, 3)])
-def test_f32_per_centre_magnitudes(oracle_mod, heads, layers):
+def test_f32_per_centre_magnitudes(oracle_mod, heads, layers, split16):
     """Centres whose features differ in magnitude by up to 2^21 each keep fp32-class relative
     accuracy against their own scale (the f16 split is scaled per centre and layer)."""
     c = 16 * heads
@@ -173,15 +204,17 @@ def test_f32_per_centre_magnitudes(oracle_mod, heads, layers):
     for i in range(rp.shape[0] - 1):
         x[rp[i]:rp[i + 1]] *= np.float32(2.0 ** k[i])
     wt = W.make_weights(layers, c, 44, np.float32)
-    y = _run(rp, x, wt, heads, 100)
+    y = _run(rp, x, wt, heads, 100, split16=split16)
     ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), heads)
     err = _per_centre_normwise(y.astype(np.float64), ref, rp)
-    print(f"variant={nga.attn_variant(1, 100, c, heads)} worst per-centre error {err:.3e}",
+    dt = nga.NGA_F32_SPLIT16 if split16 else nga.NGA_F32
+    print(f"variant={nga.attn_variant(dt, 100, c, heads)} worst per-centre error {err:.3e}",
           flush=True)
     assert err < TOL[np.float32]
 
 
-def test_f32_weight_magnitudes(oracle_mod):
+@pytest.mark.parametrize("split16", [False, True])
+def test_f32_weight_magnitudes(oracle_mod, split16):
     """Weight matrices scaled far from 1 (2^-30 .. 2^30, with non-power-of-two factors) give
     the same relative accuracy; the scales are paired so that the scores keep their size."""
     rp = W.random_rows(40, 181, 51, min_len=1)
@@ -191,16 +224,17 @@ def test_f32_weight_magnitudes(oracle_mod):
     for (l, m), s in zip([(0, 0), (0, 1), (0, 2), (0, 3), (1, 0), (1, 2), (1, 3)],
                          [2.0 ** -30 * 3, 2.0 ** 28, 2.0 ** 30, 2.0 ** -30, 0.7, 2.0 ** -12, 5.0]):
         wt[l, m] *= np.float32(s)
-    y = _run(rp, x, wt, 4, 181)
+    y = _run(rp, x, wt, 4, 181, split16=split16)
     ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), 4)
     err = _normwise(y.astype(np.float64), ref)
     print(f"normwise error {err:.3e}", flush=True)
     assert err < TOL[np.float32]
 
 
-@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float64, 32, 4, 60), (np.float64, 64, 4, 100),
-                                             (np.float32, 64, 4, 181)])
-def test_order_gather_scatter(oracle_mod, dtype, c, heads, cap):
+@pytest.mark.parametrize("dtype,c,heads,cap,split16", [
+    (np.float64, 32, 4, 60, False), (np.float64, 64, 4, 100, False), (np.float32, 64, 4, 181, False),
+    (np.float32, 64, 4, 181, True)])
+def test_order_gather_scatter(oracle_mod, dtype, c, heads, cap, split16):
     rp = W.random_rows(30, cap, 77, min_len=1)
     e = int(rp[-1])
     x = W.make_features(e, c, 78, dtype)
@@ -208,25 +242,26 @@ def test_order_gather_scatter(oracle_mod, dtype, c, heads, cap):
     perm = np.random.default_rng(80).permutation(e).astype(np.int32)  # slot s stored at perm[s]
     x2 = np.empty_like(x)
     x2[perm] = x
-    y2 = _run(rp, x2, wt, heads, cap, order=perm)
+    y2 = _run(rp, x2, wt, heads, cap, order=perm, split16=split16)
     ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), heads)
     assert _normwise(y2[perm].astype(np.float64), ref) < TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float64, 32, 4, 40), (np.float64, 128, 4, 110),
-                                             (np.float32, 64, 4, 181)])
-def test_deterministic_and_cap_independent(dtype, c, heads, cap):
+@pytest.mark.parametrize("dtype,c,heads,cap,split16", [
+    (np.float64, 32, 4, 40, False), (np.float64, 128, 4, 110, False), (np.float32, 64, 4, 181, False),
+    (np.float32, 64, 4, 181, True)])
+def test_deterministic_and_cap_independent(dtype, c, heads, cap, split16):
     rp = W.random_rows(50, cap, 91)
     e = int(rp[-1])
     x = W.make_features(e, c, 92, dtype)
     wt = W.make_weights(1, c, 93, dtype)
-    a = _run(rp, x, wt, heads, cap)
-    b = _run(rp, x, wt, heads, cap)
+    a = _run(rp, x, wt, heads, cap, split16=split16)
+    b = _run(rp, x, wt, heads, cap, split16=split16)
     assert np.array_equal(a, b)
     bigger = cap + 10  # a larger cap within the same kernel variant changes nothing
-    dt = 0 if dtype == np.float64 else 1
+    dt = nga.NGA_F64 if dtype == np.float64 else (nga.NGA_F32_SPLIT16 if split16 else nga.NGA_F32)
     assert nga.attn_variant(dt, bigger, c, heads) == nga.attn_variant(dt, cap, c, heads)
-    c2 = _run(rp, x, wt, heads, bigger)
+    c2 = _run(rp, x, wt, heads, bigger, split16=split16)
     assert np.array_equal(a, c2)
 
 
@@ -234,17 +269,23 @@ PATH_CASES = [  # (dtype, c, heads, kernel path)
     (np.float64, 16, 4, "generic_f64"),
     (np.float64, 16, 2, "fused_f64"),
     (np.float64, 64, 4, "mfma_f64"),
-    (np.float32, 16, 1, "fused_f32_d16"),
+    (np.float32, 16, 1, "fused_f32"),
+    (np.float32, 64, 4, "fused_f32"),
+    (np.float32, 16, 1, "fused_f32_split16"),
+    (np.float32, 40, 5, "generic_f32"),
 ]
 
 
 def _path_check(dtype, c, heads, cap, variant):
-    assert nga.attn_variant(0 if dtype == np.float64 else 1, cap, c, heads) == variant
+    split16 = variant.endswith("split16")
+    dt = nga.NGA_F64 if dtype == np.float64 else (nga.NGA_F32_SPLIT16 if split16 else nga.NGA_F32)
+    assert nga.attn_variant(dt, cap, c, heads) == variant
+    return split16
 
 
 @pytest.mark.parametrize("dtype,c,heads,variant", PATH_CASES)
 def test_rows_untouched_outside_centres(dtype, c, heads, variant):
-    _path_check(dtype, c, heads, 8, variant)
+    split16 = _path_check(dtype, c, heads, 8, variant)
     rp = np.array([0, 3, 3, 7], np.int64)
     x = W.make_features(10, c, 1, dtype)
     wt = W.make_weights(1, c, 2, dtype)
@@ -252,31 +293,51 @@ def test_rows_untouched_outside_centres(dtype, c, heads, variant):
     y = torch.full_like(xt, 7.0)
     ws = nga.Workspace(DEV)
     nga.block_attn_forward(torch.from_numpy(rp).to(DEV), xt, torch.from_numpy(wt).to(DEV), heads,
-                           8, y=y, ws=ws)
+                           8, y=y, ws=ws, split16=split16)
     nga.check_status(ws)
     assert torch.all(y[7:] == 7.0)
 
 
 @pytest.mark.parametrize("dtype,c,heads,variant", PATH_CASES)
 def test_row_over_cap_is_reported(dtype, c, heads, variant):
-    _path_check(dtype, c, heads, 10, variant)
+    split16 = _path_check(dtype, c, heads, 10, variant)
     rp = np.array([0, 5, 30], np.int64)
     x = W.make_features(30, c, 1, dtype)
     wt = W.make_weights(1, c, 2, dtype)
     ws = nga.Workspace(DEV)
     nga.block_attn_forward(torch.from_numpy(rp).to(DEV), torch.from_numpy(x).to(DEV),
-                           torch.from_numpy(wt).to(DEV), heads, 10, ws=ws)
+                           torch.from_numpy(wt).to(DEV), heads, 10, ws=ws, split16=split16)
     assert nga.sync_status(ws) == -4
 
 
 @pytest.mark.parametrize("dtype,c,heads,variant", PATH_CASES)
+def test_decreasing_row_ptr_is_reported(dtype, c, heads, variant):
+    """A row_ptr whose endpoints are valid but which decreases inside: the rows it would give
+    (negative length, or starting below zero) are reported as NGA_ECAP and skipped, and the
+    valid rows are still computed."""
+    split16 = _path_check(dtype, c, heads, 16, variant)
+    x = W.make_features(12, c, 1, dtype)
+    wt = W.make_weights(1, c, 2, dtype)
+    for rp in (np.array([0, 6, 3, 12], np.int64),      # centre 1 has r1 < r0
+               np.array([0, -4, 5, 12], np.int64)):    # centre 1 starts below zero
+        ws = nga.Workspace(DEV)
+        y = torch.full((12, c), 7.0, dtype=torch.float64 if dtype == np.float64 else torch.float32,
+                       device=DEV)
+        nga.block_attn_forward(torch.from_numpy(rp).to(DEV), torch.from_numpy(x).to(DEV),
+                               torch.from_numpy(wt).to(DEV), heads, 16, y=y, ws=ws,
+                               split16=split16)
+        assert nga.sync_status(ws) == -4
+
+
+@pytest.mark.parametrize("dtype,c,heads,variant", PATH_CASES)
 def test_order_out_of_range_is_reported(dtype, c, heads, variant):
-    _path_check(dtype, c, heads, 8, variant)
+    split16 = _path_check(dtype, c, heads, 8, variant)
     rp = np.array([0, 4, 8], np.int64)
     x = W.make_features(8, c, 1, dtype)
     wt = W.make_weights(1, c, 2, dtype)
     order = torch.tensor([0, 1, 2, 3, 4, 5, 6, 99], dtype=torch.int32, device=DEV)
     ws = nga.Workspace(DEV)
     nga.block_attn_forward(torch.from_numpy(rp).to(DEV), torch.from_numpy(x).to(DEV),
-                           torch.from_numpy(wt).to(DEV), heads, 8, order=order, ws=ws)
+                           torch.from_numpy(wt).to(DEV), heads, 8, order=order, ws=ws,
+                           split16=split16)
     assert nga.sync_status(ws) == -8

@@ -1,8 +1,7 @@
 """GPU LocalAtten (one query per centre over its edges) against the oracle.
 
-Normwise tolerances as for block attention (1e-12 fp64 / 2e-5 fp32).  The diamond workloads
-whole, the 65,536-atom Fe BCC workload at full size with 300 sampled centres (the oracle runs
-on the sub-CSR of those centres: a centre's output depends only on its own rows), random
+Normwise tolerances as for block attention (1e-12 fp64 / 2e-5 fp32).  All five workloads
+whole (the two Fe BCC workloads at full size after a sampled pre-check), random
 ragged rows across the kernel's 64-row LDS chunks (empty rows, one-edge rows, rows up to the
 512-neighbour cap), several layers and head counts, `order`, and the error paths.
 """
@@ -55,25 +54,34 @@ def test_diamond_workloads(oracle_mod, key):
     assert err < TOL[np.float64]
 
 
-def test_fe_bcc_65536_sampled_centres(oracle_mod):
-    w = W.WORKLOADS[4]
+@pytest.mark.parametrize("key", [4, 5])
+def test_fe_bcc_full_size_whole_output(oracle_mod, key):
+    """Both Fe BCC workloads at full size (one and two layers), every centre's output against
+    the oracle, after a sampled pre-check on 300 centres (the oracle runs on the sub-CSR of
+    those centres: a centre's output depends only on its own rows)."""
+    w = W.WORKLOADS[key]
     rp, e = _gpu_csr(w)
     n = rp.shape[0] - 1
     x = W.workload_features(w, e)
-    xc = W.make_features(n, w.c, 504, np.float32)
+    xc = W.make_features(n, w.c, 500 + key, np.float32)
     wt = W.workload_weights(w)
     y = _local(rp, xc, x, wt, w.heads)
+    assert np.all(np.isfinite(y))
     centres = np.unique(np.concatenate(
-        [[0, n - 1], np.random.default_rng(5004).choice(n, 300, replace=False)]))
+        [[0, n - 1], np.random.default_rng(5000 + key).choice(n, 300, replace=False)]))
     lens = rp[centres + 1] - rp[centres]
     sub_rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     sub_x = np.concatenate([x[rp[i]:rp[i + 1]] for i in centres])
-    ref = oracle_mod.local_atten(sub_rp, xc[centres].astype(np.float64),
-                                 sub_x.astype(np.float64), wt.astype(np.float64), w.heads)
-    err = _normwise(y[centres].astype(np.float64), ref)
-    print(f"workload {w.name} N={n} E={e}: sampled normwise error {err:.3e}", flush=True)
+    ref_s = oracle_mod.local_atten(sub_rp, xc[centres].astype(np.float64),
+                                   sub_x.astype(np.float64), wt.astype(np.float64), w.heads)
+    err_s = _normwise(y[centres].astype(np.float64), ref_s)
+    print(f"workload {w.name} N={n} E={e}: sampled normwise error {err_s:.3e}", flush=True)
+    assert err_s < TOL[np.float32]
+    ref = oracle_mod.local_atten(rp, xc.astype(np.float64), x.astype(np.float64),
+                                 wt.astype(np.float64), w.heads)
+    err = _normwise(y.astype(np.float64), ref)
+    print(f"workload {w.name}: whole-output normwise error {err:.3e}", flush=True)
     assert err < TOL[np.float32]
-    assert np.all(np.isfinite(y))
 
 
 CASES = [

@@ -1,10 +1,9 @@
 """GPU neighbour rows and destination CSR against the oracle: bit-exact.
 
-Whole-CSR comparisons on every input the oracle finishes in seconds (the
-three diamond workloads, ideal lattices with exact distance ties, tiny boxes
-with many images, random orthorhombic boxes, hand cases), sampled rows plus
-whole-list invariants on the two Fe BCC workloads at full size, and the
-device-detected error paths.
+Whole-CSR comparisons on all five workloads (the three diamond workloads and
+the two Fe BCC workloads at full size), ideal lattices with exact distance
+ties, tiny boxes with many images, random orthorhombic boxes and hand cases,
+plus the device-detected error paths.
 """
 import numpy as np
 import pytest
@@ -55,42 +54,23 @@ def test_diamond_workloads_bitexact(oracle_mod, key):
     assert g["n_edges"] == pos.shape[0] * w.sel
 
 
-def _row_keys(vec, col, shift):
-    d = vec
-    r2 = (d[:, 0] * d[:, 0] + d[:, 1] * d[:, 1]) + d[:, 2] * d[:, 2]
-    return r2
-
-
 @pytest.mark.parametrize("key", [4, 5])
-def test_fe_bcc_full_size_sampled_rows(oracle_mod, key):
-    """Full-size Fe BCC lists: sampled rows bit-exact vs the oracle, invariants everywhere."""
+def test_fe_bcc_full_size_whole_csr(oracle_mod, key):
+    """Full-size Fe BCC lists: the whole CSR (row_ptr, col, shift, dst, edge_vec) bit-exact
+    against the brute-force oracle, plus the relation's symmetry (rows are never cut here)."""
     w = W.WORKLOADS[key]
     pos, box = W.workload_positions(w)
     n = pos.shape[0]
     print(f"workload {w.name} N={n}", flush=True)
     g = _gpu_csr(pos, box, w.rcut, w.sel)
-    rp, col, shift, vec = g["row_ptr"], g["col"], g["shift"], g["edge_vec"]
-    rng = np.random.default_rng(1000 + key)
-    sample = np.unique(np.concatenate([[0, n - 1], rng.choice(n, 40, replace=False)]))
-    for i in sample:
-        c, s, v, r2, nw = oracle_mod.nl_row(pos, box, w.rcut, w.sel, int(i))
-        sl = slice(rp[i], rp[i + 1])
-        assert np.array_equal(col[sl], c), i
-        assert np.array_equal(shift[sl], s), i
-        assert np.array_equal(vec[sl], v), i
-    # invariants over the whole list
+    ref = oracle_mod.nl_full(pos, box, w.rcut, w.sel)
+    print(f"oracle E={ref[0][-1]}, GPU E={g['n_edges']}", flush=True)
+    _assert_same_csr(g, ref)
+    rp, col, shift = g["row_ptr"], g["col"], g["shift"]
     counts = np.diff(rp)
-    assert counts.max() <= w.sel and counts.min() >= 1
-    r2 = _row_keys(vec, col, shift)
-    assert np.all(r2 < w.rcut * w.rcut)
+    assert counts.max() < w.sel and counts.min() >= 1
+    # the untruncated relation is symmetric: (i, j, n) <-> (j, i, -n)
     same_row = np.repeat(np.arange(n), counts)
-    nxt = np.arange(len(col) - 1)
-    inrow = same_row[nxt] == same_row[nxt + 1]
-    lo_key = col.astype(np.int64)
-    ordered = (r2[nxt] < r2[nxt + 1]) | ((r2[nxt] == r2[nxt + 1]) & (lo_key[nxt] < lo_key[nxt + 1]))
-    assert np.all(ordered[inrow])
-    # rows are never truncated here, so the relation must be symmetric: (i, j, n) <-> (j, i, -n)
-    assert counts.max() < w.sel
     code = lambda a, b, s: ((a * n + b) * 1000 + (s[:, 0] + 10) * 100 + (s[:, 1] + 10) * 10
                             + (s[:, 2] + 10))
     fwd = np.sort(code(same_row.astype(np.int64), col.astype(np.int64), shift.astype(np.int64)))

@@ -1,6 +1,7 @@
 """GPU smooth attention (per-segment softmax rescale by sum_j e_j / D~) against the oracle.
 
-Every kernel path the dispatcher can take -- the fused fp32 and fp64 kernels, the fp64
+Every kernel path the dispatcher can take -- the fused fp32 kernel (fp32 matrix cores, and the
+f16 split-pair arithmetic asked for by NGA_F32_SPLIT16), the fused fp64 kernel, the fp64
 matrix-core path and the generic path in both precisions -- against oracle.attn_smooth, normwise
 (1e-12 fp64 / 2e-5 fp32), over several layers, with ln D~ drawn per layer, edge and head.
 Plus: ln D~ equal to each segment's log-sum-exp reproduces the vanilla forward; the `order`
@@ -26,13 +27,13 @@ def _normwise(y, ref):
     return float(np.max(np.abs(y - ref)) / np.max(np.abs(ref)))
 
 
-def _run(row_ptr, x, w, heads, cap, ldt=None, order=None, ws=None, check=True):
+def _run(row_ptr, x, w, heads, cap, ldt=None, order=None, ws=None, check=True, split16=False):
     ws = ws or nga.Workspace(DEV)
     y = nga.block_attn_forward(
         torch.from_numpy(row_ptr).to(DEV), torch.from_numpy(x).to(DEV),
         torch.from_numpy(w).to(DEV), heads, cap,
         order=None if order is None else torch.from_numpy(order).to(DEV), ws=ws,
-        log_dtilde=None if ldt is None else torch.from_numpy(ldt).to(DEV))
+        log_dtilde=None if ldt is None else torch.from_numpy(ldt).to(DEV), split16=split16)
     if check:
         nga.check_status(ws, "attention")
     return y.cpu().numpy()
@@ -75,9 +76,12 @@ def _log_dtilde(oracle_mod, row_ptr, x, w, heads, dtype, seed):
 
 CASES = [
     # dtype, n_centres, max_len, c, heads, layers, seed, expected variant
-    (np.float32, 40, 181, 64, 4, 2, 1, "fused_f32_d16"),
-    (np.float32, 40, 96, 32, 2, 3, 2, "fused_f32_d16"),
-    (np.float32, 30, 40, 16, 1, 1, 3, "fused_f32_d16"),
+    (np.float32, 40, 181, 64, 4, 2, 1, "fused_f32"),
+    (np.float32, 40, 96, 32, 2, 3, 2, "fused_f32"),
+    (np.float32, 30, 40, 16, 1, 1, 3, "fused_f32"),
+    (np.float32, 40, 181, 64, 4, 2, 1, "fused_f32_split16"),
+    (np.float32, 40, 96, 32, 2, 3, 2, "fused_f32_split16"),
+    (np.float32, 30, 40, 16, 1, 1, 3, "fused_f32_split16"),
     (np.float64, 30, 120, 128, 4, 2, 4, "mfma_f64"),
     (np.float64, 40, 40, 32, 4, 2, 5, "fused_f64"),
     (np.float64, 30, 90, 64, 4, 2, 8, "mfma_f64"),
@@ -97,9 +101,10 @@ def test_smooth_matches_oracle(oracle_mod, dtype, nc, maxlen, c, heads, layers, 
     x = W.make_features(e, c, seed + 100, dtype)
     wt = W.make_weights(layers, c, seed + 200, dtype)
     ldt = _log_dtilde(oracle_mod, rp, x, wt, heads, dtype, seed + 300)
-    dt = nga.NGA_F64 if dtype == np.float64 else nga.NGA_F32
+    split16 = variant.endswith("split16")
+    dt = nga.NGA_F64 if dtype == np.float64 else (nga.NGA_F32_SPLIT16 if split16 else nga.NGA_F32)
     assert nga.attn_variant(dt, maxlen, c, heads) == variant
-    y = _run(rp, x, wt, heads, maxlen, ldt=ldt)
+    y = _run(rp, x, wt, heads, maxlen, ldt=ldt, split16=split16)
     ref = oracle_mod.attn_smooth(rp, x.astype(np.float64), wt.astype(np.float64), heads,
                                  ldt.astype(np.float64))
     err = _normwise(y.astype(np.float64), ref)
@@ -107,16 +112,17 @@ def test_smooth_matches_oracle(oracle_mod, dtype, nc, maxlen, c, heads, layers, 
     assert err < TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float32, 64, 4, 181), (np.float64, 32, 4, 60),
-                                               (np.float64, 64, 4, 90), (np.float64, 20, 2, 40)])
-def test_dtilde_equal_to_segment_sum_is_vanilla(dtype, c, heads, cap):
+@pytest.mark.parametrize("dtype,c,heads,cap,split16", [
+    (np.float32, 64, 4, 181, False), (np.float32, 64, 4, 181, True), (np.float64, 32, 4, 60, False),
+    (np.float64, 64, 4, 90, False), (np.float64, 20, 2, 40, False)])
+def test_dtilde_equal_to_segment_sum_is_vanilla(dtype, c, heads, cap, split16):
     rp = W.random_rows(30, cap, 11, min_len=1)
     e = int(rp[-1])
     x = W.make_features(e, c, 12, dtype)
     wt = W.make_weights(1, c, 13, dtype)
     ldt = _segment_lse(rp, x, wt[0], heads)[None].astype(dtype)
-    ys = _run(rp, x, wt, heads, cap, ldt=ldt)
-    yv = _run(rp, x, wt, heads, cap)
+    ys = _run(rp, x, wt, heads, cap, ldt=ldt, split16=split16)
+    yv = _run(rp, x, wt, heads, cap, split16=split16)
     assert _normwise(ys.astype(np.float64), yv.astype(np.float64)) < TOL[dtype]
 
 
@@ -146,9 +152,10 @@ def _rowwise(y, ref):
     return float(np.max(num[keep] / den[keep]))
 
 
-@pytest.mark.parametrize("dtype,c,heads,cap", [(np.float32, 64, 4, 120), (np.float32, 32, 2, 60),
-                                               (np.float64, 32, 4, 60)])
-def test_factors_far_from_one_match_oracle_row_by_row(oracle_mod, dtype, c, heads, cap):
+@pytest.mark.parametrize("dtype,c,heads,cap,split16", [
+    (np.float32, 64, 4, 120, False), (np.float32, 32, 2, 60, False), (np.float32, 64, 4, 120, True),
+    (np.float32, 32, 2, 60, True), (np.float64, 32, 4, 60, False)])
+def test_factors_far_from_one_match_oracle_row_by_row(oracle_mod, dtype, c, heads, cap, split16):
     """Rescale factors sum_j e_j / D~ of e^40, 1, e^-30 and e^60 on the heads of the same
     query rows, then factors spread over e^-60 .. e^60 row by row: every edge row of y must
     match the oracle to the tolerance relative to that row's own magnitude."""
@@ -164,7 +171,7 @@ def test_factors_far_from_one_match_oracle_row_by_row(oracle_mod, dtype, c, head
     spread = np.random.default_rng(44).uniform(-60.0, 60.0, (e, 1))
     for shift in (per_head[None, :], spread):
         ldt = (lse + shift)[None].astype(dtype)
-        y = _run(rp, x, wt, heads, cap, ldt=ldt)
+        y = _run(rp, x, wt, heads, cap, ldt=ldt, split16=split16)
         ref = oracle_mod.attn_smooth(rp, x.astype(np.float64), wt.astype(np.float64), heads,
                                      ldt.astype(np.float64))
         assert np.all(np.isfinite(y))
