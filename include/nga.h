@@ -7,6 +7,8 @@
  *   nl_build            O(N) cell-list neighbour rows under periodic boundaries
  *   nl_refine           the same rows from cached candidate rows (reuse)
  *   nl_max_displacement the device-side test for that reuse
+ *   nl_build_static     nl_build without a workspace, for callers that cannot
+ *                       allocate
  *   nl_build_batch      neighbour rows of many structures in one launch sequence
  *   edge_csr            those rows as a destination CSR with image shifts
  *   block_attn_forward  block-dense multi-head attention through the CSR
@@ -70,7 +72,8 @@ enum {
     NGA_EDTYPE = -5,     /* unsupported dtype */
     NGA_EWORKSPACE = -6, /* workspace missing or smaller than the query returned */
     NGA_EHIP = -7,       /* HIP runtime error */
-    NGA_EINDEX = -8      /* an index in device data is out of range */
+    NGA_EINDEX = -8,     /* an index in device data is out of range */
+    NGA_ETOOBIG = -9     /* more scratch than the allocation-free entry point holds */
 };
 
 /* Feature dtypes of the attention calls.
@@ -124,6 +127,36 @@ size_t nl_build_workspace_bytes(int64_t n_atoms, const double* h_box, double rcu
 int nl_build(const double* pos, int64_t n_atoms, const double* h_box, double rcut, int32_t sel,
              int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, size_t ws_bytes,
              void* stream);
+
+/* Device scratch held by nl_build_static, per GPU, for the life of the process. */
+#define NGA_STATIC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * nl_build for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same rows, bit for bit, with no workspace argument.  Its scratch is a
+ * library-held device array of NGA_STATIC_SCRATCH_BYTES per GPU (kept until
+ * the process ends); the first call on a GPU looks up that array's address.
+ * The call allocates and frees nothing.
+ *
+ * Arguments as nl_build, except:
+ * status    device buffer of at least 256 bytes owned by the caller, zero-
+ *           filled once before its first use: device-detected errors
+ *           (NGA_EBOX, NGA_EROWCAP) are recorded in it as in a workspace
+ *           header, and nga_sync_status(status, stream) returns and clears
+ *           them.
+ * Limit: nl_build_workspace_bytes(n_atoms, h_box, rcut) must not exceed
+ * NGA_STATIC_SCRATCH_BYTES (about 40 bytes per atom plus 12 per cell: some
+ * 400,000 atoms at the density of the Fe BCC workloads, 262,000 when the box
+ * has the most cells the build uses, two per atom), else NGA_ETOOBIG before
+ * anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch: calls that can overlap on
+ * one GPU (different streams, or threads without ordering) race and must not
+ * be issued; calls ordered on one stream are safe.
+ */
+int nl_build_static(const double* pos, int64_t n_atoms, const double* h_box, double rcut,
+                    int32_t sel, int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* status,
+                    void* stream);
 
 /* Workspace bytes nl_build_batch needs (0 if the structures are invalid). */
 size_t nl_build_batch_workspace_bytes(int32_t n_structs, const int64_t* h_atom_ptr,

@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     nl_build,
     local_attn_forward,
     nl_build_batch,
+    nl_build_static,
     nl_build_workspace_bytes,
     nl_max_displacement,
     nl_refine,

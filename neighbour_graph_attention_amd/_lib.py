@@ -17,7 +17,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnga.so")
 
 NGA_OK, NGA_EINVAL, NGA_EBOX, NGA_EROWCAP, NGA_ECAP, NGA_EDTYPE, NGA_EWORKSPACE, NGA_EHIP, \
-    NGA_EINDEX = 0, -1, -2, -3, -4, -5, -6, -7, -8
+    NGA_EINDEX, NGA_ETOOBIG = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+STATIC_SCRATCH_BYTES = 16 << 20
 NGA_F64, NGA_F32, NGA_F32_SPLIT16 = 0, 1, 2
 ROW_CAP = 512
 
@@ -27,7 +28,7 @@ EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "
            "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward",
            "nga_step_graph_create", "nga_step_graph_launch", "nga_step_graph_destroy",
            "nl_refine", "nl_max_displacement", "nl_build_batch_workspace_bytes",
-           "nl_build_batch")
+           "nl_build_batch", "nl_build_static")
 
 
 class NGAError(RuntimeError):
@@ -65,6 +66,8 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward_smooth.restype = ctypes.c_int
     lib.block_attn_forward_smooth.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32,
                                               vp, vp, vp, vp, vp, sz, vp]
+    lib.nl_build_static.restype = ctypes.c_int
+    lib.nl_build_static.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, vp, vp]
     lib.nl_build_batch_workspace_bytes.restype = sz
     lib.nl_build_batch_workspace_bytes.argtypes = [i32, vp, vp, dbl]
     lib.nl_build_batch.restype = ctypes.c_int
@@ -201,6 +204,32 @@ def nl_build(pos: torch.Tensor, box, rcut: float, sel: int, *, nbr=None, nbr_shi
     rc = lib.nl_build(_ptr(pos), n, _box3(box), float(rcut), int(sel), _ptr(nbr), _ptr(nbr_shift),
                       _ptr(nnei), ws.ptr(), ws.nbytes, _stream(dev))
     _check(rc, "nl_build")
+    return nbr, nbr_shift, nnei
+
+
+def nl_build_static(pos: torch.Tensor, box, rcut: float, sel: int, status: Workspace, *,
+                    nbr=None, nbr_shift=None, nnei=None):
+    """nl_build without a workspace (the library's static device scratch; allocation-free on the
+    library side).  Device-detected errors go to `status` (a Workspace of at least 256 bytes,
+    read with sync_status / check_status).  Returns (nbr, nbr_shift, nnei)."""
+    lib = load()
+    dev = pos.device
+    n = pos.shape[0]
+    _need(pos, "pos", torch.float64, (n, 3), dev)
+    if nbr is None:
+        nbr = torch.empty((n, sel), dtype=torch.int32, device=dev)
+    if nbr_shift is None:
+        nbr_shift = torch.empty((n, sel, 3), dtype=torch.int32, device=dev)
+    if nnei is None:
+        nnei = torch.empty((n,), dtype=torch.int32, device=dev)
+    _need(nbr, "nbr", torch.int32, (n, sel), dev)
+    _need(nbr_shift, "nbr_shift", torch.int32, (n, sel, 3), dev)
+    _need(nnei, "nnei", torch.int32, (n,), dev)
+    if status.nbytes < 256 or status.device != dev:
+        raise ValueError("status must be a Workspace of at least 256 bytes on the device")
+    rc = lib.nl_build_static(_ptr(pos), n, _box3(box), float(rcut), int(sel), _ptr(nbr),
+                             _ptr(nbr_shift), _ptr(nnei), status.ptr(), _stream(dev))
+    _check(rc, "nl_build_static")
     return nbr, nbr_shift, nnei
 
 

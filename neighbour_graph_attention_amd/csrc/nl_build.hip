@@ -28,6 +28,8 @@
 // plain evaluation of the same formula.
 #pragma clang fp contract(off)
 
+#include <mutex>
+
 #include "nga_internal.h"
 
 #include <algorithm>
@@ -750,10 +752,12 @@ bool short_segments(int64_t n, const Geom& g) {
     return seg_est <= 96.0;
 }
 
+// ws: the scratch regions (carved after a 256-byte header); status: the word that collects
+// device-detected errors (the workspace's own header word for nl_build).
 int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t sel,
-              int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, hipStream_t s) {
+              int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws, uint32_t* status,
+              hipStream_t s) {
     WsLayout w = carve(ws, n, g);
-    uint32_t* status = &static_cast<WsHeader*>(ws)->status;
     const int ni = (int)n;
     int rc;
     if (n <= kSmallAtoms && g.ncells <= kSmallCells) {
@@ -1149,5 +1153,57 @@ extern "C" int nl_build(const double* pos, int64_t n_atoms, const double* h_box,
     if (!pos || !nbr || !nbr_shift || !nnei) return NGA_EINVAL;
     if (!ws || ws_bytes < nga::carve(nullptr, n_atoms, g).bytes) return NGA_EWORKSPACE;
     return nga::launch_nl(pos, n_atoms, g, rcut, sel, nbr, nbr_shift, nnei, ws,
+                          &static_cast<nga::WsHeader*>(ws)->status,
+                          static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------------------
+// nl_build_static: nl_build for callers that cannot allocate.  Its scratch (cell counts, the
+// cell scan, per-atom cell and slot, the cell-sorted atoms) lives in this file-scope device
+// array, one copy per GPU, held until the process ends.  In host code `scratch` only names
+// the symbol: its device address on the current GPU comes from hipGetSymbolAddress, taken
+// once per device and kept in scratch_dev; that address is what the kernels receive.  Every
+// call on a GPU reuses that GPU's array, so calls that overlap on one GPU race; nothing in it
+// has to start at zero (the counting kernels clear what they count into).
+static __device__ __align__(256) unsigned char scratch[NGA_STATIC_SCRATCH_BYTES];
+
+namespace nga {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NGA_EHIP;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NGA_EHIP;
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return NGA_OK;
+}
+
+}  // namespace
+}  // namespace nga
+
+extern "C" int nl_build_static(const double* pos, int64_t n_atoms, const double* h_box,
+                               double rcut, int32_t sel, int32_t* nbr, int32_t* nbr_shift,
+                               int32_t* nnei, void* status, void* stream) {
+    nga::Geom g;
+    if (!nga::make_geom(n_atoms, h_box, rcut, &g)) return NGA_EINVAL;
+    if (sel < 1) return NGA_EINVAL;
+    if (nga::carve(nullptr, n_atoms, g).bytes > (size_t)NGA_STATIC_SCRATCH_BYTES)
+        return NGA_ETOOBIG;
+    if (n_atoms == 0) return NGA_OK;
+    if (!pos || !nbr || !nbr_shift || !nnei || !status) return NGA_EINVAL;
+    void* ws = nullptr;
+    if (int rc = nga::static_scratch(&ws)) return rc;
+    return nga::launch_nl(pos, n_atoms, g, rcut, sel, nbr, nbr_shift, nnei, ws,
+                          &static_cast<nga::WsHeader*>(status)->status,
                           static_cast<hipStream_t>(stream));
 }

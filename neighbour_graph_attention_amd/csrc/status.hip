@@ -17,6 +17,8 @@ extern "C" const char* nga_strerror(int status) {
         case NGA_EWORKSPACE: return "workspace missing or too small";
         case NGA_EHIP: return "HIP runtime error";
         case NGA_EINDEX: return "an index in device data is out of range";
+        case NGA_ETOOBIG:
+            return "the problem needs more scratch than the allocation-free entry point holds";
         default: return "unknown status";
     }
 }

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_strerror_covers_codes():
-    for code in range(0, -9, -1):
+    for code in range(0, -10, -1):
         assert nga.strerror(code) != "unknown status"
     assert nga.strerror(-99) == "unknown status"
 
@@ -208,6 +208,28 @@ def test_nl_refine_and_displacement_reject_bad_arguments():
     assert call(n=0) == L.NGA_OK
     assert lib.nl_max_displacement(FAKE, FAKE, 10, box, None, None) == L.NGA_EINVAL
     assert lib.nl_max_displacement(None, FAKE, 10, box, FAKE, None) == L.NGA_EINVAL
+
+
+def test_nl_build_static_rejects_bad_arguments_and_sizes():
+    """The allocation-free nl_build checks its arguments and its scratch limit on the host,
+    before it looks up its scratch or launches anything."""
+    lib = nga.load()
+    box = (ctypes.c_double * 3)(10.0, 10.0, 10.0)
+
+    def call(pos=FAKE, n=10, box=box, rcut=2.0, sel=8, nbr=FAKE, sh=FAKE, nn=FAKE, st=FAKE):
+        return lib.nl_build_static(pos, n, box, rcut, sel, nbr, sh, nn, st, None)
+
+    assert call(rcut=0.0) == L.NGA_EINVAL
+    assert call(n=-1) == L.NGA_EINVAL
+    assert call(sel=0) == L.NGA_EINVAL
+    assert call(box=None) == L.NGA_EINVAL
+    assert call(pos=None) == L.NGA_EINVAL
+    assert call(st=None) == L.NGA_EINVAL    # the caller's status block is required
+    assert call(n=0) == L.NGA_OK            # nothing to do
+    big = (ctypes.c_double * 3)(400.0, 400.0, 400.0)
+    assert lib.nl_build_workspace_bytes(2_000_000, big, 8.0) > L.STATIC_SCRATCH_BYTES
+    assert call(n=2_000_000, box=big, rcut=8.0) == L.NGA_ETOOBIG
+    assert nga.strerror(L.NGA_ETOOBIG) != "unknown status"
 
 
 def test_nl_build_batch_rejects_bad_structures():
