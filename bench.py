@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--split16", action="store_true",
                     help="also time the NGA_F32_SPLIT16 arithmetic (f16 hi/lo pairs) on the same "
                          "inputs and report its time and its difference from the fp32 output")
+    ap.add_argument("--no-gather-scatter", action="store_true",
+                    help="skip the standalone block_gather / block_scatter leg (the padded "
+                         "per-centre block of the workload's features and its scatter back, "
+                         "timed after the steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
@@ -438,6 +442,51 @@ def main():
                      "achieved_gbs": loc_bytes / (loc_ms * 1e-3) / 1e9,
                      "frac_hbm": loc_bytes / (loc_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
+    gs_rec = None
+    if not args.no_gather_scatter:
+        # The (nloc, nnei_cap, c) block of the pages' block-dense route, materialised by the
+        # standalone copies: gather reads the edge rows and writes every block row (padding
+        # included), scatter reads the valid block rows and writes the edge rows.
+        ws_gs = nga.Workspace(dev)
+        blk = torch.empty((n, w.sel, w.c), dtype=x.dtype, device=dev)
+        yg = torch.empty_like(x)
+        rp_t = csr_out["row_ptr"]
+        nga.block_gather(rp_t, x, w.sel, block=blk, ws=ws_gs)
+        nga.block_scatter(rp_t, blk, yg, ws=ws_gs)
+        nga.check_status(ws_gs, "block_gather / block_scatter")
+        if not torch.equal(yg, x):
+            raise RuntimeError("block_scatter(block_gather(x)) differs from x")
+
+        def timed_copy(fn):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.steps)]
+            for _ in range(max(1, args.warmup)):
+                fn()
+            for e0, e1 in evs:
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize(dev)
+            return robust([e0.elapsed_time(e1) for e0, e1 in evs])
+
+        g_ms = timed_copy(lambda: nga.block_gather(rp_t, x, w.sel, block=blk, ws=ws_gs))
+        s_ms = timed_copy(lambda: nga.block_scatter(rp_t, blk, yg, ws=ws_gs))
+        nga.check_status(ws_gs, "block_gather / block_scatter")
+        es = x.element_size()
+        g_bytes = float(e * w.c * es + n * w.sel * w.c * es + 8 * (n + 1))
+        s_bytes = float(2 * e * w.c * es + 8 * (n + 1))
+
+        def rate(nbytes, ms):
+            gbs = nbytes / (ms["mean"] * 1e-3) / 1e9
+            return {"algorithmic_bytes": nbytes, "ms": ms, "achieved_gbs": gbs,
+                    "frac": gbs / PEAK_HBM_GBS}
+
+        gs_rec = {"block_shape": [n, w.sel, w.c],
+                  "gather": rate(g_bytes, g_ms), "scatter": rate(s_bytes, s_ms),
+                  "bytes_basis": "gather: E*c*s read + N*cap*c*s written (padding rows "
+                                 "included) + row_ptr; scatter: 2*E*c*s + row_ptr"}
+        del blk, yg
+
     split_rec = None
     if args.split16 and w.dtype == "f32":
         v16 = nga.attn_variant(nga.NGA_F32_SPLIT16, w.sel, w.c, w.heads)
@@ -536,6 +585,8 @@ def main():
         rec["pair_axis"] = pair_rec
     if split_rec is not None:
         rec["split16"] = split_rec
+    if gs_rec is not None:
+        rec["gather_scatter"] = gs_rec
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, pos_np, box, rp, x_np, wt_np, args.cpu_seconds)
     else:

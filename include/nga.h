@@ -14,6 +14,7 @@
  *   block_attn_forward  block-dense multi-head attention through the CSR
  *   block_attn_forward_smooth  the same with a per-segment softmax rescale
  *   local_attn_forward  LocalAtten: one query per centre over its edges
+ *   block_gather / block_scatter  the padded per-centre block on its own
  *   pair_attn_forward   the same attention by the ragged pair-axis route
  *                       (a measured comparator)
  *   nga_step_graph_*    one step (nl_build, edge_csr, block_attn_forward)
@@ -361,6 +362,44 @@ int local_attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order,
                        int64_t n_centres, int64_t n_edges, int32_t c, int32_t n_heads,
                        int32_t n_layers, const void* weights, const void* xc, const void* x,
                        void* yc, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The padded per-centre block, gathered and scattered on its own            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The (nloc, nnei_max, c) block of [P2] "Proposed fix: block-dense attention
+ * on the graph", materialised: for every centre i with n_i = row_ptr[i+1] -
+ * row_ptr[i] edges (e_k = order ? order[row_ptr[i] + k] : row_ptr[i] + k),
+ *   block[i][k][:] = x[e_k][:]   for k < n_i,
+ *   block[i][k][:] = 0           for n_i <= k < nnei_cap.
+ * block_attn_forward never builds this tensor (its kernels gather straight
+ * into on-chip memory); these two calls exist to measure and inspect the
+ * gather / scatter boundary on its own.  Both are exact copies.
+ *
+ * dtype      NGA_F64 or NGA_F32 (element size of x, y and block).
+ * row_ptr, order, n_edges as block_attn_forward; n_centres < 2^31.
+ * nnei_cap   block rows per centre; a row longer than it is NGA_ECAP.
+ * x          [n_edges][c] (gather input); block [n_centres][nnei_cap][c].
+ * ws         workspace of at least 256 bytes (its status word), zero-filled
+ *            once.
+ * Device-detected: NGA_ECAP (row_ptr decreasing, outside [0, n_edges] or a
+ * row over nnei_cap: that centre's block is zero-filled / not scattered),
+ * NGA_EINDEX (order out of range).
+ */
+int block_gather(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                 int64_t n_edges, int32_t nnei_cap, int32_t c, const void* x, void* block,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The inverse: y[e_k][:] = block[i][k][:] for every centre i and k < n_i
+ * ([P2] "Proposed fix": scatter back to the edge axis).  Padding rows of the
+ * block are not read; rows of y that belong to no centre are left as they
+ * are.  Arguments and errors as block_gather; block and y must not alias.
+ */
+int block_scatter(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                  int64_t n_edges, int32_t nnei_cap, int32_t c, const void* block, void* y,
+                  void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Ragged pair-axis attention (measured comparator)                          */

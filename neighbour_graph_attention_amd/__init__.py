@@ -7,7 +7,10 @@ Python face of libnga.so, the C-ABI library declared in include/nga.h:
 * ``block_attn_forward``: block-dense multi-head attention through the CSR;
 * ``local_attn_forward``: LocalAtten, one query per centre over its edges;
 * ``pair_attn_forward``: the same attention by the ragged pair-axis route, a
-  measured comparator.
+  measured comparator;
+* ``block_gather`` / ``block_scatter``: the padded per-centre block on its own;
+* ``nl_build_static``: ``nl_build`` without a workspace, for callers that
+  cannot allocate.
 
 Importing the package loads the library and fails loudly if it has not been
 built (``neighbour_graph_attention_amd._build.build()``).
@@ -24,6 +27,8 @@ from ._lib import (  # noqa: F401
     attn_variant,
     block_attn_forward,
     block_attn_workspace_bytes,
+    block_gather,
+    block_scatter,
     check_status,
     edge_csr,
     load,

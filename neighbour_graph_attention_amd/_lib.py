@@ -28,7 +28,7 @@ EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "
            "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward",
            "nga_step_graph_create", "nga_step_graph_launch", "nga_step_graph_destroy",
            "nl_refine", "nl_max_displacement", "nl_build_batch_workspace_bytes",
-           "nl_build_batch", "nl_build_static")
+           "nl_build_batch", "nl_build_static", "block_gather", "block_scatter")
 
 
 class NGAError(RuntimeError):
@@ -66,6 +66,10 @@ def load() -> ctypes.CDLL:
     lib.block_attn_forward_smooth.restype = ctypes.c_int
     lib.block_attn_forward_smooth.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, i32, i32,
                                               vp, vp, vp, vp, vp, sz, vp]
+    for name in ("block_gather", "block_scatter"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_int, vp, vp, i64, i64, i32, i32, vp, vp, vp, sz, vp]
     lib.nl_build_static.restype = ctypes.c_int
     lib.nl_build_static.argtypes = [vp, i64, vp, dbl, i32, vp, vp, vp, vp, vp]
     lib.nl_build_batch_workspace_bytes.restype = sz
@@ -351,6 +355,59 @@ def block_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Te
                                            _ptr(weights), _ptr(x), _ptr(log_dtilde), _ptr(y),
                                            ws.ptr(), ws.nbytes, _stream(dev))
         _check(rc, "block_attn_forward_smooth")
+    return y
+
+
+def _copy_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float64:
+        return NGA_F64
+    if t.dtype == torch.float32:
+        return NGA_F32
+    raise TypeError(f"features must be float64 or float32, got {t.dtype}")
+
+
+def block_gather(row_ptr: torch.Tensor, x: torch.Tensor, nnei_cap: int, *,
+                 order: torch.Tensor | None = None, block: torch.Tensor | None = None,
+                 ws: Workspace | None = None):
+    """The padded per-centre block [n_centres][nnei_cap][c] of x's rows (zeros past each
+    centre's row count)."""
+    lib = load()
+    dev = x.device
+    e, c = x.shape
+    n_centres = row_ptr.shape[0] - 1
+    _need(row_ptr, "row_ptr", torch.int64, (n_centres + 1,), dev)
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if order is not None:
+        _need(order, "order", torch.int32, (order.shape[0],), dev)
+    if block is None:
+        block = torch.empty((n_centres, int(nnei_cap), c), dtype=x.dtype, device=dev)
+    _need(block, "block", x.dtype, (n_centres, int(nnei_cap), c), dev)
+    ws = _ws(ws, dev, 256)
+    rc = lib.block_gather(_copy_dtype(x), _ptr(row_ptr), _ptr(order), n_centres, e,
+                          int(nnei_cap), c, _ptr(x), _ptr(block), ws.ptr(), ws.nbytes,
+                          _stream(dev))
+    _check(rc, "block_gather")
+    return block
+
+
+def block_scatter(row_ptr: torch.Tensor, block: torch.Tensor, y: torch.Tensor, *,
+                  order: torch.Tensor | None = None, ws: Workspace | None = None):
+    """Write the valid rows of block [n_centres][cap][c] back into y [E][c] (in place)."""
+    lib = load()
+    dev = y.device
+    e, c = y.shape
+    n_centres, cap = block.shape[0], block.shape[1]
+    _need(row_ptr, "row_ptr", torch.int64, (n_centres + 1,), dev)
+    _need(block, "block", y.dtype, (n_centres, cap, c), dev)
+    if not y.is_contiguous():
+        raise ValueError("y must be contiguous")
+    if order is not None:
+        _need(order, "order", torch.int32, (order.shape[0],), dev)
+    ws = _ws(ws, dev, 256)
+    rc = lib.block_scatter(_copy_dtype(y), _ptr(row_ptr), _ptr(order), n_centres, e, cap, c,
+                           _ptr(block), _ptr(y), ws.ptr(), ws.nbytes, _stream(dev))
+    _check(rc, "block_scatter")
     return y
 
 

@@ -7,7 +7,9 @@ Plain, slow, obviously correct fp64 reference of what the GPU path computes:
 * ``attn_naive`` / ``attn_naive_centres``: per-centre multi-head attention in
   naive loops;
 * ``attn_pairaxis``: the same layers in the ragged pair-axis form (pairs,
-  segment softmax, index_add).
+  segment softmax, index_add);
+* ``block_gather`` / ``block_scatter``: the padded per-centre block through
+  the destination CSR and its scatter back to the edge axis.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It shares no code with the GPU
@@ -65,6 +67,10 @@ def _load():
     lib.orc_local_atten.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]
     lib.orc_attn_naive_centres.restype = ctypes.c_int
     lib.orc_attn_naive_centres.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp]
+    for name in ("orc_block_gather", "orc_block_scatter"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp]
     lib.orc_num_threads.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     _lib = lib
@@ -220,4 +226,38 @@ def attn_pairaxis(row_ptr, x, w, heads: int, order=None):
                                w.shape[0], _ptr(w), _ptr(x), _ptr(y))
     if rc != 0:
         raise ValueError("oracle attn_pairaxis failed")
+    return y
+
+
+def block_gather(row_ptr, x, cap: int, order=None):
+    """Padded per-centre block [n_centres][cap][c] of the rows of x (same dtype), zeros past
+    each centre's row count."""
+    lib = _load()
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    order = None if order is None else np.ascontiguousarray(order, dtype=np.int32)
+    x = np.ascontiguousarray(x)
+    e, c = x.shape
+    nc = row_ptr.shape[0] - 1
+    block = np.empty((nc, cap, c), dtype=x.dtype)
+    rc = lib.orc_block_gather(_ptr(row_ptr), _ptr(order), nc, e, int(cap), c, x.itemsize,
+                              _ptr(x), _ptr(block))
+    if rc != 0:
+        raise ValueError("oracle block_gather: row over cap or index out of range")
+    return block
+
+
+def block_scatter(row_ptr, block, y, order=None):
+    """Write the valid rows of block [n_centres][cap][c] back into y [E][c] (in place; rows of
+    no centre untouched); returns y."""
+    lib = _load()
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int64)
+    order = None if order is None else np.ascontiguousarray(order, dtype=np.int32)
+    block = np.ascontiguousarray(block)
+    if not (y.flags["C_CONTIGUOUS"] and y.dtype == block.dtype):
+        raise ValueError("y must be C-contiguous with the block's dtype")
+    nc, cap, c = block.shape
+    rc = lib.orc_block_scatter(_ptr(row_ptr), _ptr(order), nc, y.shape[0], cap, c,
+                               block.itemsize, _ptr(block), _ptr(y))
+    if rc != 0:
+        raise ValueError("oracle block_scatter: row over cap or index out of range")
     return y

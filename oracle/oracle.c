@@ -631,6 +631,68 @@ int orc_local_atten(const int64_t* row_ptr, const int32_t* order, int64_t n_cent
     return failed ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Block gather / scatter through the destination CSR.                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The padded per-centre block of [P2] "Proposed fix: block-dense attention
+ * on the graph": for every centre i with n_i = row_ptr[i+1] - row_ptr[i]
+ * edges, block[i][k][:] = x[e_k][:] for k < n_i (e_k = order ? order[row_ptr[i]
+ * + k] : row_ptr[i] + k) and block[i][k][:] = 0 for n_i <= k < cap, the
+ * (nloc, nnei_max, c) tensor.  Elements are copied as bytes of width es
+ * (8 or 4), so the copy is exact for any dtype.  Returns 0, or -1 if a row
+ * is longer than cap or an index is out of range.
+ */
+int orc_block_gather(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                     int64_t n_edges, int32_t cap, int32_t c, int32_t es, const void* x,
+                     void* block)
+{
+    const char* xs = (const char*)x;
+    char* bs = (char*)block;
+    const size_t row = (size_t)c * es;
+    for (int64_t i = 0; i < n_centres; ++i) {
+        const int64_t n = row_ptr[i + 1] - row_ptr[i];
+        if (n < 0 || n > cap) return -1;
+        for (int64_t k = 0; k < cap; ++k) {
+            char* dst = bs + ((size_t)i * cap + k) * row;
+            if (k < n) {
+                const int64_t e = orc_edge_of(row_ptr, order, i, k);
+                if (e < 0 || e >= n_edges) return -1;
+                memcpy(dst, xs + (size_t)e * row, row);
+            } else {
+                memset(dst, 0, row);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * The inverse scatter back to the edge axis ([P2] "Proposed fix": scatter
+ * back): y[e_k][:] = block[i][k][:] for every centre i and k < n_i; rows of
+ * y that belong to no centre are left as they are, padding rows are not
+ * read.  Returns 0, or -1 as orc_block_gather.
+ */
+int orc_block_scatter(const int64_t* row_ptr, const int32_t* order, int64_t n_centres,
+                      int64_t n_edges, int32_t cap, int32_t c, int32_t es, const void* block,
+                      void* y)
+{
+    const char* bs = (const char*)block;
+    char* ys = (char*)y;
+    const size_t row = (size_t)c * es;
+    for (int64_t i = 0; i < n_centres; ++i) {
+        const int64_t n = row_ptr[i + 1] - row_ptr[i];
+        if (n < 0 || n > cap) return -1;
+        for (int64_t k = 0; k < n; ++k) {
+            const int64_t e = orc_edge_of(row_ptr, order, i, k);
+            if (e < 0 || e >= n_edges) return -1;
+            memcpy(ys + (size_t)e * row, bs + ((size_t)i * cap + k) * row, row);
+        }
+    }
+    return 0;
+}
+
 /* Threads the OpenMP loops above use (1 without OpenMP). */
 int orc_num_threads(void)
 {

@@ -210,6 +210,27 @@ def test_nl_refine_and_displacement_reject_bad_arguments():
     assert lib.nl_max_displacement(None, FAKE, 10, box, FAKE, None) == L.NGA_EINVAL
 
 
+def test_block_gather_scatter_reject_bad_arguments():
+    lib = nga.load()
+    for fn in (lib.block_gather, lib.block_scatter):
+        def call(dt=L.NGA_F32, nc=4, ne=40, cap=16, c=16, rp=FAKE, src=0x100000, dst=0x900000,
+                 ws=FAKE, wsb=256):
+            return fn(dt, rp, None, nc, ne, cap, c, ctypes.c_void_p(src), ctypes.c_void_p(dst),
+                      ws, wsb, None)
+
+        assert call(dt=L.NGA_F32_SPLIT16) == L.NGA_EDTYPE
+        assert call(dt=9) == L.NGA_EDTYPE
+        assert call(cap=0) == L.NGA_EINVAL
+        assert call(c=0) == L.NGA_EINVAL
+        assert call(nc=-1) == L.NGA_EINVAL
+        assert call(rp=None) == L.NGA_EINVAL
+        assert call(src=0) == L.NGA_EINVAL
+        assert call(dst=0x100000 + 64) == L.NGA_EINVAL        # the two arrays overlap
+        assert call(ws=None) == L.NGA_EWORKSPACE
+        assert call(wsb=128) == L.NGA_EWORKSPACE
+        assert call(nc=0) == L.NGA_OK
+
+
 def test_nl_build_static_rejects_bad_arguments_and_sizes():
     """The allocation-free nl_build checks its arguments and its scratch limit on the host,
     before it looks up its scratch or launches anything."""

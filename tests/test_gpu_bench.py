@@ -56,6 +56,10 @@ def test_bench_fp32_line_prices_the_fp32_matrix_cores():
     for k in ("step_ms", "nl_build_ms", "edge_csr_ms", "block_attn_forward_ms"):
         for stat in ("mean", "median", "trimmed_mean_10"):
             assert t[k][stat] > 0.0, (k, stat)
+    gs = d["gather_scatter"]
+    assert gs["block_shape"] == [65536, 181, 64]
+    for k in ("gather", "scatter"):
+        assert gs[k]["achieved_gbs"] > 0.0 and 0.0 < gs[k]["frac"] < 1.0
     s16 = d["split16"]
     assert s16["kernel"] == "fused_f32_split16"
     assert 0.0 < s16["normwise_diff_vs_fp32_output"] < 2e-5
