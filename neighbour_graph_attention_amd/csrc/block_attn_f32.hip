@@ -91,13 +91,21 @@ struct Lds {
 // and values follow, the heads' outputs meet in LDS for the output projection, and the
 // result is stored to y (last layer) or written back over the block rows it came from
 // (earlier layers; those rows are no longer read in this layer).
+//
+// Softmax shift.  Any shift b_j >= max_k s_jk gives the same softmax; the exact row max costs
+// a pass over the scores before the exponentials.  Instead each query row takes the
+// Cauchy-Schwarz bound b_j = |q_j| max_k |k_k| (in the base-2 units of the scaled keys), which
+// needs only the query's norm, and enters the score MFMAs as their initial accumulator, so the
+// exponentials read s_jk - b_j straight from the MFMA results.  If the bound is so loose that a
+// row's exponentials all underflow (Z < 2^-64; it takes a score range of some 64 binary orders
+// of magnitude between the bound and the true max), the wave recomputes its tile with the exact
+// max.
 template <int H, int NT, bool SMOOTH>
 __device__ __forceinline__ void centre_layer(const F32Args& A, const float* __restrict__ P,
                                              const int layer, const int64_t r0, const int n,
                                              const bool last,
                                              float (*__restrict__ sX)[Lds<H>::XS],
-                                             f4 (*__restrict__ sO)[H][64],
-                                             float (*__restrict__ sWoh)[64], const int lane,
+                                             f4 (*__restrict__ sO)[H][64], const int lane,
                                              const int h) {
     constexpr int C = 16 * H;
     constexpr int KS = C / 4;
@@ -106,7 +114,7 @@ __device__ __forceinline__ void centre_layer(const F32Args& A, const float* __re
     const int li = lane & 15;
     const float c1 = kLog2e * 0.25f;  // log2(e) / sqrt(16): the softmax in base 2
 
-    float wq[KS], wk[KS], wv[KS];
+    float wq[KS], wk[KS], wv[KS], wo[KS];
 #pragma unroll
     for (int k4 = 0; k4 < KS / 4; ++k4) {
         const f4 a = *reinterpret_cast<const f4*>(P + 0 * MAT + 4 * k4);
@@ -118,12 +126,14 @@ __device__ __forceinline__ void centre_layer(const F32Args& A, const float* __re
             wq[4 * k4 + i] = a[i];
             wk[4 * k4 + i] = b[i];
             wv[4 * k4 + i] = c[i];
-            sWoh[4 * k4 + i][lane] = d[i];  // read back by this wavefront only
+            wo[4 * k4 + i] = d[i];
         }
     }
 
-    // K^T and V of every row tile, kept in registers for the layer.
+    // K^T (scaled by c1: scores come out in base-2 units) and V of every row tile, kept in
+    // registers for the layer; kn2 = the largest squared key norm of this head.
     f4 kt[NT], vt[NT];
+    float kn2 = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
         float xo[KS];
@@ -139,9 +149,18 @@ __device__ __forceinline__ void centre_layer(const F32Args& A, const float* __re
             k = mfma4(wk[kk], xo[kk], k);
             v = mfma4(xo[kk], wv[kk], v);
         }
+        k *= c1;
         kt[t] = k;
         vt[t] = v;
+        // lane (g, i) holds channels 4g .. 4g+3 of key 16t + i
+        float k2 = k[0] * k[0] + k[1] * k[1] + k[2] * k[2] + k[3] * k[3];
+        k2 += __shfl_xor(k2, 16, 64);
+        k2 += __shfl_xor(k2, 32, 64);
+        kn2 = fmaxf(kn2, k2);
     }
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) kn2 = fmaxf(kn2, __shfl_xor(kn2, d, 64));
+    const float kmax = sqrtf(kn2);
 
     for (int qt = 0; qt < NT; ++qt) {
         f4 q = {0.f, 0.f, 0.f, 0.f};
@@ -156,37 +175,69 @@ __device__ __forceinline__ void centre_layer(const F32Args& A, const float* __re
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) q = mfma4(wq[kk], xo[kk], q);
         }
+        // lane (g, j) holds channels 4g .. 4g+3 of query j: its norm times kmax bounds every
+        // score of row j.
+        float q2 = q[0] * q[0] + q[1] * q[1] + q[2] * q[2] + q[3] * q[3];
+        q2 += __shfl_xor(q2, 16, 64);
+        q2 += __shfl_xor(q2, 32, 64);
+        float shift = sqrtf(q2) * kmax;
+        const f4 init = {-shift, -shift, -shift, -shift};
         f4 s[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            f4 acc = mfma4(kt[t][0], q[0], init);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc = mfma4(kt[t][r], q[r], acc);
+            for (int r = 1; r < 4; ++r) acc = mfma4(kt[t][r], q[r], acc);
             s[t] = acc;
         }
         // NT = ceil(n / 16), so only the last key tile can hold keys past the row end.
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             if (16 * (NT - 1) + 4 * g + r >= n) s[NT - 1][r] = -INFINITY;
-        float m = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) m = fmaxf(m, s[t][r]);
-        m = fmaxf(m, __shfl_xor(m, 16, 64));
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const float mc = m * c1;
         float z = 0.f;
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = __builtin_amdgcn_exp2f(s[t][r] * c1 - mc);
+                const float p = __builtin_amdgcn_exp2f(s[t][r]);
                 s[t][r] = p;
                 z += p;
             }
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
+        if (__builtin_expect(__any(z < 0x1p-64f), 0)) {
+            // The bound left a row's weights (nearly) all underflowed: this tile again with
+            // the exact row max as the shift.
+            float m = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc = mfma4(kt[t][r], q[r], acc);
+                s[t] = acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (16 * (NT - 1) + 4 * g + r >= n) s[NT - 1][r] = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, s[t][r]);
+            m = fmaxf(m, __shfl_xor(m, 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            shift = m;
+            z = 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = __builtin_amdgcn_exp2f(s[t][r] - m);
+                    s[t][r] = p;
+                    z += p;
+                }
+            z += __shfl_xor(z, 16, 64);
+            z += __shfl_xor(z, 32, 64);
+        }
         f4 osum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -194,14 +245,14 @@ __device__ __forceinline__ void centre_layer(const F32Args& A, const float* __re
             for (int r = 0; r < 4; ++r) osum = mfma4(vt[t][r], s[t][r], osum);
         f4 o;
         if constexpr (SMOOTH) {
-            // sum_j e_j / D~ times the softmax = exp(s_j - ln D~): the weighted sum times
-            // exp(m / sqrt(d) - ln D~) = 2^(mc - log2(e) ln D~) in place of 1 / Z.
+            // sum_j e_j / D~ times the softmax = exp(s_j / sqrt(d) - ln D~): the weighted sum
+            // (shifted by `shift` in base 2) times 2^(shift - log2(e) ln D~) in place of 1 / Z.
             const int aq = 16 * qt + li;
             float f = 0.f;
             if (aq < n) {
                 const int64_t row = A.order ? (int64_t)A.order[r0 + aq] : r0 + aq;
                 if (row >= 0 && row < A.n_edges)
-                    f = exp2f(mc - kLog2e * A.ldt[((int64_t)layer * A.n_edges + row) * H + h]);
+                    f = exp2f(shift - kLog2e * A.ldt[((int64_t)layer * A.n_edges + row) * H + h]);
             }
             o = osum * f;
         } else {
@@ -216,7 +267,7 @@ __device__ __forceinline__ void centre_layer(const F32Args& A, const float* __re
         for (int hh = 0; hh < H; ++hh) {
             const f4 oo = sO[buf][hh][lane];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yv = mfma4(sWoh[4 * hh + r][lane], oo[r], yv);
+            for (int r = 0; r < 4; ++r) yv = mfma4(wo[4 * hh + r], oo[r], yv);
         }
         const int a = 16 * qt + li;
         if (last) {
@@ -241,7 +292,6 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_kernel(F32Args A) {
     constexpr int PER = (16 * TMAX * CH + NTH - 1) / NTH;
     __shared__ __align__(16) float sX[16 * TMAX][Lds<H>::XS];
     __shared__ f4 sO[2][H][64];
-    __shared__ float sWo[H][KS][64];
 
     const int lane = threadIdx.x & 63;
     const int h = threadIdx.x >> 6;
@@ -296,7 +346,7 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f32_kernel(F32Args A) {
 #define NGA_CASE(T)                                                                       \
     case T:                                                                               \
         if constexpr (T <= TMAX)                                                          \
-            centre_layer<H, T, SMOOTH>(A, P, layer, r0, n, last, sX, sO, sWo[h], lane, h); \
+            centre_layer<H, T, SMOOTH>(A, P, layer, r0, n, last, sX, sO, lane, h);        \
         break;
         switch (nt) {
             NGA_CASE(1) NGA_CASE(2) NGA_CASE(3) NGA_CASE(4) NGA_CASE(5) NGA_CASE(6)

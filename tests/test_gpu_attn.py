@@ -213,6 +213,35 @@ def test_f32_per_centre_magnitudes(oracle_mod, heads, layers, split16):
     assert err < TOL[np.float32]
 
 
+def _rowwise(y, ref):
+    """Largest over rows of max |y_r - ref_r| / max |ref_r| (rows with ref_r = 0 skipped)."""
+    den = np.max(np.abs(ref), axis=1)
+    num = np.max(np.abs(y - ref), axis=1)
+    keep = den > 0
+    return float(np.max(num[keep] / den[keep]))
+
+
+@pytest.mark.parametrize("split16", [False, True])
+def test_f32_one_huge_key_per_centre(oracle_mod, split16):
+    """Each centre's first edge row is 1e4 in channel 0 and every other row is 0 there, with
+    identity weights: head 0's largest key norm is then some 1e4 times its scores against the
+    other queries, so a softmax shifted by |q| max|k| would underflow those rows (the fp32
+    kernel then recomputes them with the exact row max).  Every row must still match the
+    oracle to the fp32 tolerance relative to its own magnitude."""
+    rp = W.random_rows(30, 181, 61, min_len=2)
+    e = int(rp[-1])
+    x = W.make_features(e, 64, 62, np.float32)
+    x[:, 0] = 0.0
+    x[rp[:-1], 0] = 1.0e4
+    wt = np.broadcast_to(np.eye(64, dtype=np.float32), (2, 4, 64, 64)).copy()
+    y = _run(rp, x, wt, 4, 181, split16=split16)
+    ref = oracle_mod.attn_naive(rp, x.astype(np.float64), wt.astype(np.float64), 4)
+    assert np.all(np.isfinite(y))
+    err = _rowwise(y.astype(np.float64), ref)
+    print(f"split16={split16}: row-wise error {err:.3e}", flush=True)
+    assert err < TOL[np.float32]
+
+
 @pytest.mark.parametrize("split16", [False, True])
 def test_f32_weight_magnitudes(oracle_mod, split16):
     """Weight matrices scaled far from 1 (2^-30 .. 2^30, with non-power-of-two factors) give
