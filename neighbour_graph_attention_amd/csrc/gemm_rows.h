@@ -1,8 +1,11 @@
 // Row-gather / row-scatter GEMM on the vector ALUs, for any channel count and either
 // precision: out[out_rows(m)][u] = sum_{t < k} a[a_rows(m)][t] * W_{u / c}[t][u % c], with nmat
 // matrices W of [k][c] side by side in the output columns (k = c unless set).  Used by the
-// generic attention path, the pair-axis route and LocalAtten.
+// generic attention path, the pair-axis route and LocalAtten.  In fp32, without row gather or
+// scatter, the product runs on the matrix cores instead (gemm_f32_mfma_kernel).
 #pragma once
+
+#include <type_traits>
 
 #include "nga_internal.h"
 
@@ -104,8 +107,102 @@ __global__ void __launch_bounds__(256) gemm_rows_kernel(GemmArgs<T> g) {
     if (bad) raise_bits(g.status, kBitIndex);
 }
 
+// The fp32 product on the matrix cores, for the plain case (no row gather or scatter, no
+// device-side row bound): a 64-row x 64-column output tile per work-group, 16 rows per
+// wavefront as four 16x16 tiles of v_mfma_f32_16x16x4f32 (fp32 products, fp32 sums: the
+// arithmetic of the vector kernel up to summation order).  The work-group's 64 columns of
+// W' (W' = [W_0 | W_1 | ..], K x nmat c) sit in LDS transposed, k contiguous, so that a lane's
+// four k values of one column are one 16-byte read; a lane's four k values of its A row are
+// one 16-byte global load.  In MFMA step s, the k slot q of the 16x16x4 operation (lanes
+// 16 q .. 16 q + 15) carries k = k0 + 4 q + s on both operands.
+constexpr int kMfmaBM = 64, kMfmaBN = 64;
+
+template <int KT>  // K = 16 KT
+__global__ void __launch_bounds__(256) gemm_f32_mfma_kernel(GemmArgs<float> g, int64_t M) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int K = 16 * KT, LDW = K + 4;
+    __shared__ __align__(16) float sWt[kMfmaBN * LDW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n0 = blockIdx.y * kMfmaBN;
+    const int64_t m0 = (int64_t)blockIdx.x * kMfmaBM;
+    const int j = lane & 15, q = lane >> 4;
+    // A: row m0 + 16 wave + j, k = 16 kk + 4 q .. + 3 for kk < KT; loads first, then staging
+    const int64_t row = m0 + wave * 16 + j;
+    const bool live = row < M;
+    const f4* arow = reinterpret_cast<const f4*>(g.a + (live ? row : m0) * g.lda);
+    f4 av[KT];
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) av[kk] = live ? arow[4 * kk + q] : f4{0.f, 0.f, 0.f, 0.f};
+    // W': thread (column cc, k group k4) reads W'[4 k4 .. 4 k4 + 3][n0 + cc], coalesced over cc
+    for (int idx = tid; idx < K / 4 * kMfmaBN; idx += 256) {
+        const int cc = idx % kMfmaBN, k4 = idx / kMfmaBN;
+        const int u = n0 + cc, mat = u / g.c, col = u - mat * g.c;
+        const float* w = g.w + ((int64_t)mat * K + 4 * k4) * g.c + col;
+        f4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = w[e * g.c];
+        *reinterpret_cast<f4*>(&sWt[cc * LDW + 4 * k4]) = v;
+    }
+    __syncthreads();
+    f4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KT; ++kk) {
+        f4 bv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            bv[t] = *reinterpret_cast<const f4*>(&sWt[(16 * t + j) * LDW + 16 * kk + 4 * q]);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk][st], bv[t][st], acc[t], 0, 0, 0);
+    }
+    // D[i][jj] of tile t sits in lane jj + 16 (i / 4), register i % 4
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int64_t m = m0 + wave * 16 + 4 * q + r;
+        if (m < M) {
+            float* o = g.out + m * g.ldo + n0 + j;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) o[16 * t] = acc[t][r];
+        }
+    }
+}
+
+// Whether gemm_f32_mfma_kernel covers this product; its K (= 16 KT) as KT, else 0.
+inline int mfma_gemm_kt(const GemmArgs<float>& g) {
+    const int K = g.k > 0 ? g.k : g.c;
+    const int nout = g.nmat * g.c;
+    if (g.a_rows || g.out_rows || g.e_dev) return 0;
+    if (g.c % 16 != 0 || nout % kMfmaBN != 0 || g.lda % 4 != 0) return 0;
+    if ((reinterpret_cast<uintptr_t>(g.a) & 15) != 0) return 0;
+    if (K != 16 && K != 32 && K != 64 && K != 128 && K != 256) return 0;
+    return K / 16;
+}
+
+template <int KT>
+void launch_mfma_gemm(const GemmArgs<float>& g, int64_t m_bound, hipStream_t s) {
+    const int64_t M = m_bound < g.n_edges ? m_bound : g.n_edges;
+    const dim3 grid((unsigned)((M + kMfmaBM - 1) / kMfmaBM), (unsigned)(g.nmat * g.c / kMfmaBN));
+    hipLaunchKernelGGL((gemm_f32_mfma_kernel<KT>), grid, dim3(256), 0, s, g, M);
+}
+
 template <typename T>
 int launch_gemm(const GemmArgs<T>& g, int64_t m_bound, hipStream_t s) {
+    if constexpr (std::is_same<T, float>::value) {
+        if (m_bound > 0 && g.n_edges > 0 && (m_bound + kMfmaBM - 1) / kMfmaBM < 2147483647) {
+            switch (mfma_gemm_kt(g)) {
+                case 1: launch_mfma_gemm<1>(g, m_bound, s); return last_launch_status();
+                case 2: launch_mfma_gemm<2>(g, m_bound, s); return last_launch_status();
+                case 4: launch_mfma_gemm<4>(g, m_bound, s); return last_launch_status();
+                case 8: launch_mfma_gemm<8>(g, m_bound, s); return last_launch_status();
+                case 16: launch_mfma_gemm<16>(g, m_bound, s); return last_launch_status();
+                default: break;
+            }
+        }
+    }
     const int nout = g.nmat * g.c;
     dim3 grid((unsigned)((m_bound + kGemmBM - 1) / kGemmBM), (unsigned)((nout + kGemmBN - 1) / kGemmBN));
     hipLaunchKernelGGL((gemm_rows_kernel<T>), grid, dim3(256), 0, s, g);

@@ -24,6 +24,8 @@
 #include "nga_internal.h"
 #include "gemm_rows.h"
 
+#include <algorithm>
+
 namespace nga {
 
 namespace {
@@ -40,6 +42,28 @@ template <>
 __device__ inline double exp_t<double>(double v) { return exp(v); }
 template <>
 __device__ inline float exp_t<float>(float v) { return expf(v); }
+
+// Scores of the four-head kernel are kept in base-2 units in fp32 (R scaled by log2 e, so the
+// softmax exponentials are single v_exp_f32), in natural units in fp64.
+template <typename T>
+struct Base2;
+template <>
+struct Base2<float> {
+    static constexpr float scale = 1.4426950408889634f;
+    __device__ static float ex(float v) { return __builtin_amdgcn_exp2f(v); }
+};
+template <>
+struct Base2<double> {
+    static constexpr double scale = 1.0;
+    __device__ static double ex(double v) { return exp(v); }
+};
+
+// A value all lanes hold alike, moved to scalar registers.
+__device__ inline int64_t uniform64(int64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // M_h[s][u] = sum over head h's columns t of Wq[s][t] Wk[u][t] / sqrt(d): H matrices [c][c].
 template <typename T>
@@ -282,6 +306,236 @@ __global__ void __launch_bounds__(kLocalThreads) local_stream_kernel(LocalArgs<T
     if (bad_index) raise_bits(A.status, kBitIndex);
 }
 
+// Position of a work-group in its sequence of chunk tasks: centre i (rows r0 .. r0+n-1 of the
+// CSR) and the chunk starting at its row j0.  i >= n_centres ends the sequence.
+struct LocalTask {
+    int64_t i, r0, n, j0;
+};
+
+// Sum over the four lanes of a quad (lanes 4k .. 4k+3), in every lane of it: DPP quad
+// permutations, no LDS traffic.
+template <typename T>
+__device__ inline T quad_sum(T v);
+template <>
+__device__ inline float quad_sum<float>(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+    return v;
+}
+template <>
+__device__ inline double quad_sum<double>(double v) {
+    // the two 32-bit halves move with the same permutation
+    int2 b = __builtin_bit_cast(int2, v);
+    int2 o;
+    o.x = __builtin_amdgcn_mov_dpp(b.x, 0xB1, 0xF, 0xF, false);
+    o.y = __builtin_amdgcn_mov_dpp(b.y, 0xB1, 0xF, 0xF, false);
+    v += __builtin_bit_cast(double, o);
+    b = __builtin_bit_cast(int2, v);
+    o.x = __builtin_amdgcn_mov_dpp(b.x, 0x4E, 0xF, 0xF, false);
+    o.y = __builtin_amdgcn_mov_dpp(b.y, 0x4E, 0xF, 0xF, false);
+    return v + __builtin_bit_cast(double, o);
+}
+
+// The streaming pass for four heads and rows of CV 16-byte vectors (CV = 4, 8 or 16: c = 16,
+// 32 or 64 in fp32, 8, 16 or 32 in fp64), as a persistent kernel.  Work-group b takes centres
+// b, b + G, b + 2G, ... (G work-groups, as many as the device holds at once); its chunks of up
+// to 64 rows follow one another across those centres, and the next chunk's loads (with the R
+// of a centre whose first chunk it is) are in flight, in registers, while the current one is
+// processed.  The chunk goes to one of two LDS buffers and each LDS row is read once per step
+// for all four heads, since LDS bandwidth, not HBM, is what the per-head layout ran out of:
+//   scores    four threads per row (row tid / 4, quarter tid % 4 of its vectors) form partial
+//             dot products against R_0 .. R_3, summed over the quad with DPP moves;
+//   softmax   wavefront h: running max and sum of head h over the chunk's rows (lane j);
+//   sums      thread (vector column t, row partition p) accumulates U_0 .. U_3 of column t over
+//             rows p, p + NPART, ... of every chunk, all four heads from one read of the row;
+//             at the centre's end the partitions are summed through LDS.
+template <typename T, int CV, bool ORD>
+__global__ void __launch_bounds__(kLocalThreads) local_stream_h4_kernel(LocalArgs<T> A) {
+    typedef typename Vec<T>::type V;
+    constexpr int EV = Vec<T>::n;
+    constexpr int H = 4;
+    constexpr int CH = kLocalChunk;                // rows per chunk
+    constexpr int SXV = CV + 1;                    // padded LDS row stride in vectors
+    constexpr int QV = CV / 4;                     // vectors per quarter row (scores)
+    constexpr int NPART = kLocalThreads / CV;      // row partitions of the weighted sums
+    constexpr int PER = CH * CV / kLocalThreads;   // chunk vectors per thread
+    static_assert(QV >= 1 && PER >= 1 && PER * kLocalThreads == CH * CV, "shape");
+    __shared__ V sX[2][CH * SXV];
+    __shared__ V sR[H * CV];
+    __shared__ __align__(16) T sS[CH][H];          // scores, then weights, row-major
+    __shared__ T sAl[H], sZ[H];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t N = A.n_centres, G = gridDim.x;
+    bool bad_index = false;
+
+    // Task values are alike in all lanes; they are kept in scalar registers.
+    auto first_chunk = [&](int64_t i) -> LocalTask {
+        for (; i < N; i += G) {
+            const int64_t r0 = uniform64(A.row_ptr[i]), r1 = uniform64(A.row_ptr[i + 1]);
+            if (r0 < 0 || r1 < r0 || r1 > A.n_edges) {
+                if (tid == 0) raise_bits(A.status, kBitCap);
+                continue;
+            }
+            if (r1 > r0) return LocalTask{i, r0, r1 - r0, 0};
+            if (tid < H * CV) reinterpret_cast<V*>(A.un + i * (H * CV * EV))[tid] = vsplat<V>(T(0));
+        }
+        return LocalTask{N, 0, 0, 0};
+    };
+    auto next_task = [&](const LocalTask& t) -> LocalTask {
+        if (t.j0 + CH < t.n) return LocalTask{t.i, t.r0, t.n, t.j0 + CH};
+        return first_chunk(t.i + G);
+    };
+    // Thread tid loads vector u of rows jr, jr + 256 / CV, ...; rows past the chunk's end
+    // repeat its last row (the loads stay unconditional; nothing reads those slots).
+    const int jr = tid / CV, u = tid % CV;
+    V pre[PER], preR = vsplat<V>(T(0));
+    auto fetch = [&](const LocalTask& t) {
+        const int last = (int)(t.n - t.j0 < CH ? t.n - t.j0 : CH) - 1;
+        if (ORD) {
+            const int32_t* ord = A.order + (t.r0 + t.j0);
+            const V* xv = reinterpret_cast<const V*>(A.x);
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int j = min(jr + q * (kLocalThreads / CV), last);
+                int64_t row = ord[j];
+                if (row < 0 || row >= A.n_edges) {
+                    bad_index = true;
+                    row = 0;
+                }
+                pre[q] = xv[row * CV + u];
+            }
+        } else {
+            const V* xv = reinterpret_cast<const V*>(A.x) + (t.r0 + t.j0) * CV;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int j = min(jr + q * (kLocalThreads / CV), last);
+                pre[q] = xv[j * CV + u];
+            }
+        }
+        if (t.j0 == 0 && tid < H * CV) preR = reinterpret_cast<const V*>(A.r + t.i * (H * CV * EV))[tid];
+    };
+
+    LocalTask cur = first_chunk(blockIdx.x);
+    if (cur.i >= N) {
+        if (bad_index) raise_bits(A.status, kBitIndex);
+        return;
+    }
+    fetch(cur);
+    LocalTask nxt = next_task(cur);
+    const int srow = tid >> 2, sq = tid & 3;             // scores: row, quarter
+    const int ut = tid % CV, upart = tid / CV;           // sums: vector column, row partition
+    T m = T(-INFINITY), z = T(0);                        // head `wave`'s running max and sum
+    V U[H];
+#pragma unroll
+    for (int hh = 0; hh < H; ++hh) U[hh] = vsplat<V>(T(0));
+    int buf = 0;
+    while (true) {
+        const int rows = (int)(cur.n - cur.j0 < CH ? cur.n - cur.j0 : CH);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) sX[buf][(jr + q * (kLocalThreads / CV)) * SXV + u] = pre[q];
+        if (cur.j0 == 0 && tid < H * CV) sR[tid] = preR * Base2<T>::scale;
+        if (nxt.i < N) fetch(nxt);
+        __syncthreads();
+        // Scores of row srow for the four heads: quarter sq of its vectors, then the quad sum.
+        {
+            T sc[H];
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) {
+                V acc = vsplat<V>(T(0));
+#pragma unroll
+                for (int u = 0; u < QV; ++u)
+                    acc += sX[buf][srow * SXV + sq * QV + u] * sR[hh * CV + sq * QV + u];
+                T v = acc[0];
+#pragma unroll
+                for (int e = 1; e < EV; ++e) v += acc[e];
+                sc[hh] = quad_sum<T>(v);
+            }
+            if (sq == 0 && srow < rows) {
+                // one 16-byte (fp32) or two 16-byte (fp64) store of the row's four scores
+#pragma unroll
+                for (int hh = 0; hh < H; ++hh) sS[srow][hh] = sc[hh];
+            }
+        }
+        __syncthreads();
+        // Online softmax of head `wave` over the chunk's rows (lane j, row j).
+        {
+            const T s = lane < rows ? sS[lane][wave] : T(-INFINITY);
+            T mc = s;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const T o = __shfl_xor(mc, off, 64);
+                mc = o > mc ? o : mc;
+            }
+            const T mnew = mc > m ? mc : m;
+            const T p = lane < rows ? Base2<T>::ex(s - mnew) : T(0);
+            T zc = p;
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) zc += __shfl_xor(zc, off, 64);
+            const T alpha = Base2<T>::ex(m - mnew);  // 0 at a centre's first chunk
+            z = z * alpha + zc;
+            m = mnew;
+            if (lane < rows) sS[lane][wave] = p;
+            if (lane == 0) {
+                sAl[wave] = alpha;
+                sZ[wave] = z;
+            }
+        }
+        __syncthreads();
+        // Weighted sums of column ut over rows upart, upart + NPART, ..., all heads at once.
+        {
+            T al[H];
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) al[hh] = sAl[hh];
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) U[hh] = U[hh] * al[hh];
+            for (int j = upart; j < rows; j += NPART) {
+                const V xv = sX[buf][j * SXV + ut];
+#pragma unroll
+                for (int hh = 0; hh < H; ++hh) U[hh] += sS[j][hh] * xv;
+            }
+        }
+        if (cur.j0 + CH >= cur.n) {
+            // The centre's last chunk: sum the row partitions and store U_h / Z_h.  Shuffles
+            // first fold a wavefront's partitions down to four (none when CV = 16), then the
+            // 16 that remain go through LDS, over the other chunk buffer, which nothing reads
+            // until the next chunk is written there.
+#pragma unroll
+            for (int off = 32; off >= 4 * CV; off >>= 1) {
+#pragma unroll
+                for (int hh = 0; hh < H; ++hh)
+#pragma unroll
+                    for (int e = 0; e < EV; ++e) U[hh][e] += __shfl_xor(U[hh][e], off, 64);
+            }
+            V* part = &sX[buf ^ 1][0];  // [16][H][CV] vectors; 64 CV <= CH (CV + 1)
+            if (lane < 4 * CV) {
+                const int pp = wave * 4 + lane / CV;
+#pragma unroll
+                for (int hh = 0; hh < H; ++hh) part[(pp * H + hh) * CV + ut] = U[hh];
+            }
+            __syncthreads();
+            if (tid < H * CV) {
+                const int hh = tid / CV, t = tid % CV;
+                V acc = vsplat<V>(T(0));
+#pragma unroll
+                for (int pp = 0; pp < 16; ++pp) acc += part[(pp * H + hh) * CV + t];
+                reinterpret_cast<V*>(A.un + cur.i * (H * CV * EV))[tid] = acc / sZ[hh];
+            }
+            m = T(-INFINITY);
+            z = T(0);
+#pragma unroll
+            for (int hh = 0; hh < H; ++hh) U[hh] = vsplat<V>(T(0));
+            // the partials' space is the next chunk's buffer: all threads must be done with it
+            __syncthreads();
+        }
+        buf ^= 1;
+        if (nxt.i >= N) break;
+        cur = nxt;
+        nxt = next_task(cur);
+    }
+    if (bad_index) raise_bits(A.status, kBitIndex);
+}
+
 // LDS bytes of the streaming kernel for `chunk` rows per chunk.
 size_t local_lds_bytes(int c, int heads, int chunk, size_t es) {
     const size_t row = (size_t)c * es + 16;  // one padded row
@@ -300,6 +554,33 @@ int local_chunk_rows(int c, int heads, size_t es) {
     for (int rows = kLocalChunk; rows >= 1; --rows)
         if (local_lds_bytes(c, heads, rows, es) <= kLocalLds) return rows;
     return 0;
+}
+
+// Work-groups of a persistent kernel: as many as the current device holds at once (resident
+// work-groups per compute unit for this kernel, from its registers and LDS, times the units).
+int64_t resident_groups(const void* kernel, int threads) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    return (int64_t)per_cu * cus;
+}
+
+template <typename T, int CV, bool ORD>
+void launch_stream_h4_o(const LocalArgs<T>& a, hipStream_t s) {
+    const void* k = reinterpret_cast<const void*>(&local_stream_h4_kernel<T, CV, ORD>);
+    const dim3 grid((unsigned)std::min<int64_t>(a.n_centres, resident_groups(k, kLocalThreads)));
+    hipLaunchKernelGGL((local_stream_h4_kernel<T, CV, ORD>), grid, dim3(kLocalThreads), 0, s, a);
+}
+
+template <typename T, int CV>
+void launch_stream_h4(const LocalArgs<T>& a, hipStream_t s) {
+    if (a.order) launch_stream_h4_o<T, CV, true>(a, s);
+    else launch_stream_h4_o<T, CV, false>(a, s);
 }
 
 struct LocalWs {
@@ -360,7 +641,12 @@ int run_local(const int64_t* row_ptr, const int32_t* order, int64_t n_centres, i
         LocalArgs<T> a{row_ptr, order, R, x, Un, n_centres, n_edges, c, heads, chunk, status};
         const int nv = hc / Vec<T>::n;
         const int loads = (chunk * (c / Vec<T>::n) + kLocalThreads - 1) / kLocalThreads;
-        if (nv <= kLocalThreads && loads <= 4)
+        const int cvec = c / Vec<T>::n;
+        if (heads == 4 && (cvec == 4 || cvec == 8 || cvec == 16)) {
+            if (cvec == 4) launch_stream_h4<T, 4>(a, s);
+            else if (cvec == 8) launch_stream_h4<T, 8>(a, s);
+            else launch_stream_h4<T, 16>(a, s);
+        } else if (nv <= kLocalThreads && loads <= 4)
             hipLaunchKernelGGL((local_stream_kernel<T, 1, 4>), dim3((unsigned)n_centres),
                                dim3(kLocalThreads), lds, s, a);
         else
