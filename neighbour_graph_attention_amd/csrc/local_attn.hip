@@ -44,17 +44,22 @@ template <>
 __device__ inline float exp_t<float>(float v) { return expf(v); }
 
 // Scores of the four-head kernel are kept in base-2 units in fp32 (R scaled by log2 e, so the
-// softmax exponentials are single v_exp_f32), in natural units in fp64.
+// softmax exponentials are single v_exp_f32), in natural units in fp64.  `lead` bounds how far
+// a later chunk's score may exceed the running shift before the shift is raised: weights up
+// to 2^30 (fp32) or e^20 (fp64) leave every sum far from overflow and lose no relative
+// precision, and a centre's shift then rarely changes after its first chunk.
 template <typename T>
 struct Base2;
 template <>
 struct Base2<float> {
     static constexpr float scale = 1.4426950408889634f;
+    static constexpr float lead = 30.0f;
     __device__ static float ex(float v) { return __builtin_amdgcn_exp2f(v); }
 };
 template <>
 struct Base2<double> {
     static constexpr double scale = 1.0;
+    static constexpr double lead = 20.0;
     __device__ static double ex(double v) { return exp(v); }
 };
 
@@ -312,43 +317,38 @@ struct LocalTask {
     int64_t i, r0, n, j0;
 };
 
-// Sum over the four lanes of a quad (lanes 4k .. 4k+3), in every lane of it: DPP quad
-// permutations, no LDS traffic.
-template <typename T>
-__device__ inline T quad_sum(T v);
-template <>
-__device__ inline float quad_sum<float>(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-    return v;
+// Lane value of the quad partner (this lane xor 1 or xor 2): a DPP quad permutation.
+template <int X>
+__device__ inline float quad_xor(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 X == 1 ? 0xB1 : 0x4E, 0xF, 0xF, true));
 }
-template <>
-__device__ inline double quad_sum<double>(double v) {
-    // the two 32-bit halves move with the same permutation
+template <int X>
+__device__ inline double quad_xor(double v) {
     int2 b = __builtin_bit_cast(int2, v);
-    int2 o;
-    o.x = __builtin_amdgcn_mov_dpp(b.x, 0xB1, 0xF, 0xF, false);
-    o.y = __builtin_amdgcn_mov_dpp(b.y, 0xB1, 0xF, 0xF, false);
-    v += __builtin_bit_cast(double, o);
-    b = __builtin_bit_cast(int2, v);
-    o.x = __builtin_amdgcn_mov_dpp(b.x, 0x4E, 0xF, 0xF, false);
-    o.y = __builtin_amdgcn_mov_dpp(b.y, 0x4E, 0xF, 0xF, false);
-    return v + __builtin_bit_cast(double, o);
+    b.x = __builtin_amdgcn_update_dpp(0, b.x, X == 1 ? 0xB1 : 0x4E, 0xF, 0xF, true);
+    b.y = __builtin_amdgcn_update_dpp(0, b.y, X == 1 ? 0xB1 : 0x4E, 0xF, 0xF, true);
+    return __builtin_bit_cast(double, b);
 }
 
 // The streaming pass for four heads and rows of CV 16-byte vectors (CV = 4, 8 or 16: c = 16,
 // 32 or 64 in fp32, 8, 16 or 32 in fp64), as a persistent kernel.  Work-group b takes centres
 // b, b + G, b + 2G, ... (G work-groups, as many as the device holds at once); its chunks of up
-// to 64 rows follow one another across those centres, and the next chunk's loads (with the R
-// of a centre whose first chunk it is) are in flight, in registers, while the current one is
-// processed.  The chunk goes to one of two LDS buffers and each LDS row is read once per step
-// for all four heads, since LDS bandwidth, not HBM, is what the per-head layout ran out of:
+// to 64 rows follow one another across those centres, and the next chunk's loads are in
+// flight, in registers, while the current one is processed.  Chunks alternate between two LDS
+// buffers, each row is read from LDS once per step for all four heads, and a chunk takes two
+// barriers:
 //   scores    four threads per row (row tid / 4, quarter tid % 4 of its vectors) form partial
-//             dot products against R_0 .. R_3, summed over the quad with DPP moves;
-//   softmax   wavefront h: running max and sum of head h over the chunk's rows (lane j);
+//             dot products against R_0 .. R_3; two DPP exchanges inside the quad leave each
+//             lane with the full score of one head, whose weight exp(s - m_h) it computes and
+//             stores.  The shift m_h is held by every thread: 0 at a centre's start, raised
+//             only when a score passes it by more than `lead` (or lowered when a centre's first
+//             chunk has no score within `lead` below it), in a rare step that takes the exact
+//             maximum and rescales what was summed so far.
 //   sums      thread (vector column t, row partition p) accumulates U_0 .. U_3 of column t over
 //             rows p, p + NPART, ... of every chunk, all four heads from one read of the row;
-//             at the centre's end the partitions are summed through LDS.
+//             at the centre's end the partitions, and the lanes' parts of each normaliser,
+//             are summed through LDS.
 template <typename T, int CV, bool ORD>
 __global__ void __launch_bounds__(kLocalThreads) local_stream_h4_kernel(LocalArgs<T> A) {
     typedef typename Vec<T>::type V;
@@ -360,10 +360,13 @@ __global__ void __launch_bounds__(kLocalThreads) local_stream_h4_kernel(LocalArg
     constexpr int NPART = kLocalThreads / CV;      // row partitions of the weighted sums
     constexpr int PER = CH * CV / kLocalThreads;   // chunk vectors per thread
     static_assert(QV >= 1 && PER >= 1 && PER * kLocalThreads == CH * CV, "shape");
+    static_assert(CH * H == kLocalThreads, "one thread per (row, head) score");
     __shared__ V sX[2][CH * SXV];
     __shared__ V sR[H * CV];
-    __shared__ __align__(16) T sS[CH][H];          // scores, then weights, row-major
-    __shared__ T sAl[H], sZ[H];
+    __shared__ __align__(16) T sS[CH][H];          // weights (scores in the rescaling step)
+    __shared__ T sM[H], sAl[H], sZ[4][H];
+    __shared__ __align__(4) uint8_t sFlag[4];      // per wave: bit 0 a score above m + lead,
+                                                   // bit 1 a score at or above m - lead
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t N = A.n_centres, G = gridDim.x;
@@ -387,7 +390,7 @@ __global__ void __launch_bounds__(kLocalThreads) local_stream_h4_kernel(LocalArg
         return first_chunk(t.i + G);
     };
     // Thread tid loads vector u of rows jr, jr + 256 / CV, ...; rows past the chunk's end
-    // repeat its last row (the loads stay unconditional; nothing reads those slots).
+    // repeat its last row (the loads stay unconditional; those rows get weight 0).
     const int jr = tid / CV, u = tid % CV;
     V pre[PER], preR = vsplat<V>(T(0));
     auto fetch = [&](const LocalTask& t) {
@@ -424,82 +427,122 @@ __global__ void __launch_bounds__(kLocalThreads) local_stream_h4_kernel(LocalArg
     fetch(cur);
     LocalTask nxt = next_task(cur);
     const int srow = tid >> 2, sq = tid & 3;             // scores: row, quarter
+    const int hq = 2 * (sq & 1) + (sq >> 1);             // the head whose score this lane ends with
     const int ut = tid % CV, upart = tid / CV;           // sums: vector column, row partition
-    T m = T(-INFINITY), z = T(0);                        // head `wave`'s running max and sum
+    T m[H];                                              // shifts, alike in every thread
+    T zl = T(0);                                         // this lane's part of Z_hq
     V U[H];
 #pragma unroll
-    for (int hh = 0; hh < H; ++hh) U[hh] = vsplat<V>(T(0));
+    for (int hh = 0; hh < H; ++hh) {
+        m[hh] = T(0);
+        U[hh] = vsplat<V>(T(0));
+    }
     int buf = 0;
     while (true) {
         const int rows = (int)(cur.n - cur.j0 < CH ? cur.n - cur.j0 : CH);
+        const bool fresh = cur.j0 == 0;  // a centre's first chunk
 #pragma unroll
         for (int q = 0; q < PER; ++q) sX[buf][(jr + q * (kLocalThreads / CV)) * SXV + u] = pre[q];
-        if (cur.j0 == 0 && tid < H * CV) sR[tid] = preR * Base2<T>::scale;
+        if (fresh && tid < H * CV) sR[tid] = preR * Base2<T>::scale;
         if (nxt.i < N) fetch(nxt);
         __syncthreads();
-        // Scores of row srow for the four heads: quarter sq of its vectors, then the quad sum.
+        // Score of row srow for head hq, and its weight.
+        const bool valid = srow < rows;
+        T sv, p;
         {
+            V xq[QV];
+#pragma unroll
+            for (int u2 = 0; u2 < QV; ++u2) xq[u2] = sX[buf][srow * SXV + sq * QV + u2];
             T sc[H];
 #pragma unroll
             for (int hh = 0; hh < H; ++hh) {
-                V acc = vsplat<V>(T(0));
+                T v = T(0);
 #pragma unroll
-                for (int u = 0; u < QV; ++u)
-                    acc += sX[buf][srow * SXV + sq * QV + u] * sR[hh * CV + sq * QV + u];
-                T v = acc[0];
+                for (int u2 = 0; u2 < QV; ++u2) {
+                    const V rv = sR[hh * CV + sq * QV + u2];
 #pragma unroll
-                for (int e = 1; e < EV; ++e) v += acc[e];
-                sc[hh] = quad_sum<T>(v);
+                    for (int e = 0; e < EV; ++e) v = fma(xq[u2][e], rv[e], v);
+                }
+                sc[hh] = v;
             }
-            if (sq == 0 && srow < rows) {
-                // one 16-byte (fp32) or two 16-byte (fp64) store of the row's four scores
+            // quad transpose-sum: after the xor-1 step lane bit 0 selects heads {0,1} or {2,3},
+            // after the xor-2 step lane bit 1 selects one of the pair
+            const bool b0 = sq & 1, b1 = sq & 2;
+            const T k0 = b0 ? sc[2] : sc[0], k1 = b0 ? sc[3] : sc[1];
+            const T g0 = b0 ? sc[0] : sc[2], g1 = b0 ? sc[1] : sc[3];
+            const T t0 = k0 + quad_xor<1>(g0), t1 = k1 + quad_xor<1>(g1);
+            const T kk = b1 ? t1 : t0, gg = b1 ? t0 : t1;
+            sv = kk + quad_xor<2>(gg);
+            T mh = m[0];
 #pragma unroll
-                for (int hh = 0; hh < H; ++hh) sS[srow][hh] = sc[hh];
-            }
+            for (int hh = 1; hh < H; ++hh) mh = hq == hh ? m[hh] : mh;
+            p = valid ? Base2<T>::ex(sv - mh) : T(0);
+            const bool over = valid && sv > mh + Base2<T>::lead;
+            const bool near = valid && sv >= mh - Base2<T>::lead;
+            const bool any_over = __any(over), any_near = __any(near);
+            if (lane == 0) sFlag[wave] = (uint8_t)((any_over ? 1 : 0) | (any_near ? 2 : 0));
+            sS[srow][hq] = p;
         }
         __syncthreads();
-        // Online softmax of head `wave` over the chunk's rows (lane j, row j).
         {
-            const T s = lane < rows ? sS[lane][wave] : T(-INFINITY);
-            T mc = s;
+            const uint32_t fl = *reinterpret_cast<const uint32_t*>(sFlag);
+            if ((fl & 0x01010101u) != 0u || (fresh && (fl & 0x02020202u) == 0u)) {
+                // Rare: new shifts from the exact maxima (over the chunk, and the old shift
+                // after a centre's first chunk), and the sums so far rescaled.
+                sS[srow][hq] = valid ? sv : T(-INFINITY);
+                __syncthreads();
+                if (lane < H) {
+                    // lanes 0..3 of every wave find the same four maxima; wave 0 writes them
+                    const int hh = lane;
+                    T mc = T(-INFINITY);
+                    for (int j = 0; j < rows; ++j) mc = sS[j][hh] > mc ? sS[j][hh] : mc;
+                    T mold = m[0];
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const T o = __shfl_xor(mc, off, 64);
-                mc = o > mc ? o : mc;
-            }
-            const T mnew = mc > m ? mc : m;
-            const T p = lane < rows ? Base2<T>::ex(s - mnew) : T(0);
-            T zc = p;
+                    for (int h2 = 1; h2 < H; ++h2) mold = hh == h2 ? m[h2] : mold;
+                    const T mnew = fresh ? mc : (mc > mold ? mc : mold);
+                    if (wave == 0) {
+                        sM[hh] = mnew;
+                        sAl[hh] = fresh ? T(1) : Base2<T>::ex(mold - mnew);
+                    }
+                }
+                __syncthreads();
 #pragma unroll
-            for (int off = 32; off > 0; off >>= 1) zc += __shfl_xor(zc, off, 64);
-            const T alpha = Base2<T>::ex(m - mnew);  // 0 at a centre's first chunk
-            z = z * alpha + zc;
-            m = mnew;
-            if (lane < rows) sS[lane][wave] = p;
-            if (lane == 0) {
-                sAl[wave] = alpha;
-                sZ[wave] = z;
+                for (int hh = 0; hh < H; ++hh) {
+                    m[hh] = sM[hh];
+                    U[hh] = U[hh] * sAl[hh];
+                }
+                T mh = m[0], al = sAl[0];
+#pragma unroll
+                for (int hh = 1; hh < H; ++hh) {
+                    mh = hq == hh ? m[hh] : mh;
+                    al = hq == hh ? sAl[hh] : al;
+                }
+                zl *= al;
+                p = valid ? Base2<T>::ex(sv - mh) : T(0);
+                sS[srow][hq] = p;  // the maxima are taken: the scores are read no more
+                __syncthreads();
             }
         }
-        __syncthreads();
+        zl += p;
         // Weighted sums of column ut over rows upart, upart + NPART, ..., all heads at once.
-        {
-            T al[H];
 #pragma unroll
-            for (int hh = 0; hh < H; ++hh) al[hh] = sAl[hh];
+        for (int r = 0; r < CH / NPART; ++r) {
+            const int j = upart + r * NPART;
+            const V xv = sX[buf][j * SXV + ut];
 #pragma unroll
-            for (int hh = 0; hh < H; ++hh) U[hh] = U[hh] * al[hh];
-            for (int j = upart; j < rows; j += NPART) {
-                const V xv = sX[buf][j * SXV + ut];
-#pragma unroll
-                for (int hh = 0; hh < H; ++hh) U[hh] += sS[j][hh] * xv;
-            }
+            for (int hh = 0; hh < H; ++hh) U[hh] += sS[j][hh] * xv;
         }
         if (cur.j0 + CH >= cur.n) {
-            // The centre's last chunk: sum the row partitions and store U_h / Z_h.  Shuffles
-            // first fold a wavefront's partitions down to four (none when CV = 16), then the
-            // 16 that remain go through LDS, over the other chunk buffer, which nothing reads
-            // until the next chunk is written there.
+            // The centre's last chunk: sum the row partitions and the normaliser parts, store
+            // U_h / Z_h.  Shuffles first fold a wavefront's partitions down to four (none when
+            // CV = 16), then the 16 that remain go through LDS, over the other chunk buffer,
+            // which nothing reads until the next chunk is written there.
+            {  // Z parts: lanes with equal tid % 4 hold the same head
+                T zw = zl;
+#pragma unroll
+                for (int off = 32; off >= 4; off >>= 1) zw += __shfl_xor(zw, off, 64);
+                if (lane < 4) sZ[wave][hq] = zw;
+            }
 #pragma unroll
             for (int off = 32; off >= 4 * CV; off >>= 1) {
 #pragma unroll
@@ -519,12 +562,15 @@ __global__ void __launch_bounds__(kLocalThreads) local_stream_h4_kernel(LocalArg
                 V acc = vsplat<V>(T(0));
 #pragma unroll
                 for (int pp = 0; pp < 16; ++pp) acc += part[(pp * H + hh) * CV + t];
-                reinterpret_cast<V*>(A.un + cur.i * (H * CV * EV))[tid] = acc / sZ[hh];
+                const T z = (sZ[0][hh] + sZ[1][hh]) + (sZ[2][hh] + sZ[3][hh]);
+                reinterpret_cast<V*>(A.un + cur.i * (H * CV * EV))[tid] = acc * (T(1) / z);
             }
-            m = T(-INFINITY);
-            z = T(0);
+            zl = T(0);
 #pragma unroll
-            for (int hh = 0; hh < H; ++hh) U[hh] = vsplat<V>(T(0));
+            for (int hh = 0; hh < H; ++hh) {
+                m[hh] = T(0);
+                U[hh] = vsplat<V>(T(0));
+            }
             // the partials' space is the next chunk's buffer: all threads must be done with it
             __syncthreads();
         }

@@ -117,6 +117,54 @@ def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, see
     assert np.all(y[0] == 0.0)  # the empty centre
 
 
+def _first_layer_scores(rp, xc, x, w, heads, i):
+    """Scores of centre i's rows in the first layer, [rows][heads], natural units."""
+    c = x.shape[1]
+    d = c // heads
+    q = xc[i] @ w[0, 0]
+    k = x[rp[i]:rp[i + 1]] @ w[0, 1]
+    return np.stack([k[:, h * d:(h + 1) * d] @ q[h * d:(h + 1) * d] for h in range(heads)],
+                    axis=1) / np.sqrt(d)
+
+
+@pytest.mark.parametrize("dtype,amp", [(np.float64, 8.0), (np.float32, 4.0)])
+def test_large_scores_move_the_shift(oracle_mod, dtype, amp):
+    """Scores far from 0: the streaming kernel's shift starts at 0 and is raised (a later
+    chunk's score more than 20 natural units, 30 base-2 units, above it) or lowered (a
+    centre's first chunk with every score more than that below it) in a separate step.  The
+    premise that both happen is checked on the inputs."""
+    c, heads = 64 if dtype == np.float32 else 32, 4
+    rp = W.random_rows(40, 200, 31, min_len=1)
+    lens = np.diff(rp)
+    lens[:4] = [200, 130, 65, 64]
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    e = int(rp[-1])
+    x = W.make_features(e, c, 32, np.float64) * amp
+    xc = W.make_features(40, c, 33, np.float64) * amp
+    wt = W.make_weights(1, c, 34, np.float64)
+    # centre 1: every row the same vector, far along one direction: each head's scores are
+    # all equal, some heads' far below 0
+    v = np.random.default_rng(35).normal(size=c)
+    x[rp[1]:rp[2]] = v * (60.0 / np.linalg.norm(v)) * amp
+    lead = 20.0 if dtype == np.float64 else 30.0 / np.log2(np.e)
+    raised = lowered = False
+    for i in range(40):
+        s = _first_layer_scores(rp, xc, x, wt, heads, i)
+        first = s[:64]
+        lowered |= bool(np.any(first.max(axis=0) < -lead))
+        if s.shape[0] > 64:
+            later = s[64:]
+            raised |= bool(np.any(later.max(axis=0) > np.maximum(first.max(axis=0), 0.0) + lead))
+    assert raised and lowered, (raised, lowered)
+    y = _local(rp, xc.astype(dtype), x.astype(dtype), wt.astype(dtype), heads)
+    ref = oracle_mod.local_atten(rp, xc.astype(dtype).astype(np.float64),
+                                 x.astype(dtype).astype(np.float64), wt.astype(dtype).astype(np.float64),
+                                 heads)
+    err = _normwise(y.astype(np.float64), ref)
+    print(f"{dtype.__name__} amp={amp}: {err:.3e}", flush=True)
+    assert err < TOL[dtype]
+
+
 def test_order_gather(oracle_mod):
     rp = W.random_rows(30, 90, 77, min_len=1)
     e = int(rp[-1])
