@@ -604,18 +604,6 @@ int local_chunk_rows(int c, int heads, size_t es) {
 
 // Work-groups of a persistent kernel: as many as the current device holds at once (resident
 // work-groups per compute unit for this kernel, from its registers and LDS, times the units).
-int64_t resident_groups(const void* kernel, int threads) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-        cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
-        per_cu < 1)
-        per_cu = 1;
-    return (int64_t)per_cu * cus;
-}
-
 template <typename T, int CV, bool ORD>
 void launch_stream_h4_o(const LocalArgs<T>& a, hipStream_t s) {
     const void* k = reinterpret_cast<const void*>(&local_stream_h4_kernel<T, CV, ORD>);
