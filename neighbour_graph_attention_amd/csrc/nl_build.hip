@@ -44,14 +44,17 @@ constexpr int kNlWaves = kNlBlock / 64;
 constexpr int kMaxReach = 5;     // stencil reach (cells) per side
 constexpr double kCellSlack = 1e-9;  // cells are at least rcut * (1 + slack) wide
 constexpr int kMaxCellsPerAxis = 1024;
+constexpr int64_t kTrimMinAtoms = 512;  // smaller systems keep whole-cell stencils
 
 struct Geom {
     double L[3];
     double inv_h[3];
+    double h[3];
     int nc[3];
     int reach[3];
     int stencil;
     int64_t ncells;
+    int trim;  // > 0: cells of at least rcut / 2, per-centre stencils of reach `trim`
 };
 
 // Cells per axis: as many as keep the cell edge >= rcut * (1 + slack), capped so that the
@@ -59,7 +62,31 @@ struct Geom {
 // within rcut * (1 + slack): k = ceil(rcut * (1 + slack) / h).  Binning rounds positions
 // to cells with an error of a few ulps of L, far below the slack, so no pair within rcut is
 // missed.
-bool make_geom(int64_t n_atoms, const double* box, double rcut, Geom* g) {
+//
+// With `trim`, a single structure whose box holds at least five cells of edge rcut / 2 per
+// axis is binned into those cells instead (reach 2, or 1 where capping made them wider), and
+// selection takes each centre's own stencil: only the cells whose nearest point can be within
+// rcut of that centre (select_trim_kernel).
+bool make_geom_cells(int64_t n_atoms, const double* box, double rcut, double div, Geom* g);
+
+bool make_geom(int64_t n_atoms, const double* box, double rcut, Geom* g, bool trim = false) {
+    if (trim && make_geom_cells(n_atoms, box, rcut, 2.0, g)) {
+        int k = 1;
+        for (int a = 0; a < 3; ++a) k = std::max(k, g->reach[a]);
+        bool ok = k <= 2;
+        for (int a = 0; a < 3; ++a) ok = ok && g->nc[a] >= 2 * k + 1;
+        if (ok && n_atoms >= kTrimMinAtoms) {
+            g->trim = k;
+            return true;
+        }
+    }
+    if (!make_geom_cells(n_atoms, box, rcut, 1.0, g)) return false;
+    g->trim = 0;
+    return true;
+}
+
+// Cells of edge at least rcut * (1 + slack) / div per axis.
+bool make_geom_cells(int64_t n_atoms, const double* box, double rcut, double div, Geom* g) {
     if (!box || !(std::isfinite(rcut) && rcut > 0.0) || n_atoms < 0 || n_atoms >= INT32_MAX)
         return false;
     const double rc = rcut * (1.0 + kCellSlack);
@@ -67,7 +94,7 @@ bool make_geom(int64_t n_atoms, const double* box, double rcut, Geom* g) {
     for (int a = 0; a < 3; ++a) {
         if (!finite_pos(box[a])) return false;
         if (box[a] / rcut > 1e7) return false;
-        double q = std::floor(box[a] / rc);
+        double q = std::floor(box[a] * div / rc);
         g->nc[a] = (int)std::max(1.0, std::min(q, (double)kMaxCellsPerAxis));
         g->L[a] = box[a];
     }
@@ -80,6 +107,7 @@ bool make_geom(int64_t n_atoms, const double* box, double rcut, Geom* g) {
     g->stencil = 1;
     for (int a = 0; a < 3; ++a) {
         double h = g->L[a] / g->nc[a];
+        g->h[a] = h;
         g->inv_h[a] = (double)g->nc[a] / g->L[a];
         int k = (int)std::ceil(rc / h);
         if (k < 1) k = 1;
@@ -728,6 +756,202 @@ select_kernel(SelectArgs A) {
     }
 }
 
+// Selection with per-centre stencils (Geom::trim = K, cells of about rcut / 2): a wavefront
+// takes one centre at a time.  Lane r < (2K+1)^2 takes stencil row (dy, dz) = (r % (2K+1) - K,
+// r / (2K+1) - K): from the centre's offset inside its own cell it finds the y and z gaps to
+// that row and then the run dx = lo .. hi of the row's cells whose nearest point is within
+// rcut (the gap grows with |dx|, so the run is contiguous).  A run is one stretch of the
+// cell-sorted array, or two where it crosses the box's x face (with their own image shifts).
+// The runs are concatenated into one list of candidate positions, read 64 to a chunk across
+// run ends: a bitmap of run starts in LDS and the run counts before each 32-bit word give
+// every lane its run.  Accepted candidates are compacted, sorted and written as in
+// select_kernel.  Any gap below the true distance only admits extra candidates, which the
+// exact r2 < rc2 test then rejects; so the run bounds take rc2 (1 + 1e-6).
+constexpr int kTrimWindow = 1024;     // candidate positions per bitmap
+constexpr int kTrimCentresPerGroup = 16;
+
+struct TrimList {
+    WaveList L;
+    uint32_t bm[kTrimWindow / 32];
+    int32_t pc[kTrimWindow / 32];
+    int2 seg[2 * 25];  // per run: (first atom slot minus its first position, shift code)
+};
+
+// Gap along one axis, in cell widths, between a point at offset f in its cell and the cell d
+// away.
+__device__ inline double cell_gap(int d, double f) {
+    return d > 0 ? (double)d - f : (d < 0 ? f + (double)(-d - 1) : 0.0);
+}
+
+__device__ inline int wave_excl_scan(int v, int lane, int* total) {
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    *total = __shfl(incl, 63, 64);
+    return incl - v;
+}
+
+template <int K>
+__global__ void __launch_bounds__(kNlBlock) select_trim_kernel(SelectArgs A) {
+    constexpr int W = 2 * K + 1, R = W * W;
+    static_assert(R <= 25, "reach");
+    extern __shared__ __align__(16) unsigned char nl_smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    TrimList& T = reinterpret_cast<TrimList*>(nl_smem)[wave];
+    WaveList& L = T.L;
+    const Geom g = A.g;
+    const int ncx = g.nc[0], ncy = g.nc[1], ncz = g.nc[2];
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int zero_code = (128 << 16) | (128 << 8) | 128;
+    const double rc2 = A.rc2, rc2s = A.rc2 * (1.0 + 1e-6);
+    const int sel = A.sel;
+    const d2* __restrict__ sa2 = reinterpret_cast<const d2*>(A.sa);
+    const int64_t* __restrict__ cs = A.cell_start;
+    const int c_end = (int)std::min<int64_t>((int64_t)A.n, ((int64_t)blockIdx.x + 1) * kTrimCentresPerGroup);
+
+    for (int ci = (int)blockIdx.x * kTrimCentresPerGroup + wave; ci < c_end; ci += kNlWaves) {
+        const d2 ci0 = sa2[2 * ci], ci1 = sa2[2 * ci + 1];
+        const int i = (int)__double_as_longlong(ci1[1]);
+        const double xi = ci0[0], yi = ci0[1], zi = ci1[0];
+        // the centre's cell, as binning found it, and its offset inside (clamped to [0, 1])
+        int cc[3];
+        double f[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            const double x = a == 0 ? xi : (a == 1 ? yi : zi);
+            const bool ok = (x >= 0.0) && (x < g.L[a]);
+            int c = ok ? (int)(x * g.inv_h[a]) : 0;
+            c = c < g.nc[a] ? c : g.nc[a] - 1;
+            cc[a] = c;
+            const double o = ok ? x * g.inv_h[a] - (double)c : 0.5;
+            f[a] = o < 0.0 ? 0.0 : (o > 1.0 ? 1.0 : o);
+        }
+        // this lane's row runs
+        int sA = 0, lA = 0, cdA = zero_code, sB = 0, lB = 0, cdB = zero_code;
+        if (lane < R) {
+            const int dy = lane % W - K, dz = lane / W - K;
+            const double gy = cell_gap(dy, f[1]) * g.h[1], gz = cell_gap(dz, f[2]) * g.h[2];
+            const double rem = rc2s - gy * gy - gz * gz;
+            if (rem > 0.0) {
+                int lo = 0, hi = 0;
+#pragma unroll
+                for (int d = 1; d <= K; ++d) {
+                    const double gp = cell_gap(d, f[0]) * g.h[0], gm = cell_gap(-d, f[0]) * g.h[0];
+                    if (gp * gp < rem) hi = d;
+                    if (gm * gm < rem) lo = -d;
+                }
+                const int ry = cc[1] + dy, rz = cc[2] + dz;
+                const int ny = floor_div(ry, ncy), nz = floor_div(rz, ncz);
+                const int rowc = ((rz - nz * ncz) * ncy + (ry - ny * ncy)) * ncx;
+                int a0 = cc[0] + lo, a1 = cc[0] + hi, b0 = 0, b1 = -1, nxb = 0;
+                if (a0 < 0) {
+                    b0 = a0 + ncx; b1 = ncx - 1; nxb = -1; a0 = 0;
+                } else if (a1 >= ncx) {
+                    b0 = 0; b1 = a1 - ncx; nxb = 1; a1 = ncx - 1;
+                }
+                sA = (int)cs[rowc + a0];
+                lA = (int)cs[rowc + a1 + 1] - sA;
+                cdA = pack_shift(0, ny, nz);
+                if (b1 >= b0) {
+                    sB = (int)cs[rowc + b0];
+                    lB = (int)cs[rowc + b1 + 1] - sB;
+                    cdB = pack_shift(nxb, ny, nz);
+                }
+            }
+        }
+        int nseg_all, total;
+        const int sid = wave_excl_scan((lA > 0) + (lB > 0), lane, &nseg_all);
+        const int base = wave_excl_scan(lA + lB, lane, &total);
+        if (lA > 0) T.seg[sid] = make_int2(sA - base, cdA);
+        if (lB > 0) T.seg[sid + (lA > 0)] = make_int2(sB - (base + lA), cdB);
+        int count = 0;
+        for (int w0 = 0; w0 < total; w0 += kTrimWindow) {  // uniform; one window in practice
+            if (lane < kTrimWindow / 32) T.bm[lane] = 0u;
+            wave_sync_lds();
+            const int bB = base + lA;
+            if (lA > 0 && base >= w0 && base < w0 + kTrimWindow)
+                atomicOr(&T.bm[(base - w0) >> 5], 1u << ((base - w0) & 31));
+            if (lB > 0 && bB >= w0 && bB < w0 + kTrimWindow)
+                atomicOr(&T.bm[(bB - w0) >> 5], 1u << ((bB - w0) & 31));
+            const int before = __popcll(__ballot(lA > 0 && base < w0)) +
+                               __popcll(__ballot(lB > 0 && bB < w0));
+            wave_sync_lds();
+            {
+                const int bits = lane < kTrimWindow / 32 ? __popc(T.bm[lane]) : 0;
+                int nb;
+                const int ex = wave_excl_scan(bits, lane, &nb);
+                if (lane < kTrimWindow / 32) T.pc[lane] = before + ex;
+            }
+            wave_sync_lds();
+            const int wend = total < w0 + kTrimWindow ? total : w0 + kTrimWindow;
+            // rounds of three 64-candidate chunks: every load is issued before the first
+            // distance is evaluated
+            for (int t0 = w0; t0 < wend; t0 += 3 * 64) {
+                double cx[3], cy[3], cz[3];
+                int cj[3], ccode[3];
+                bool live[3];
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    const int t = t0 + 64 * u + lane;
+                    live[u] = t < wend;
+                    const int p = (live[u] ? t : w0) - w0;
+                    const uint32_t word = T.bm[p >> 5];
+                    const int b = p & 31;
+                    const uint32_t upto = b == 31 ? word : (word & ((2u << b) - 1u));
+                    const int owner = T.pc[p >> 5] + __popc(upto) - 1;
+                    const int2 sg = T.seg[owner];
+                    const int a = sg.x + (live[u] ? t : w0);
+                    ccode[u] = sg.y;
+                    const d2 v0 = sa2[2 * a], v1 = sa2[2 * a + 1];
+                    cx[u] = v0[0];
+                    cy[u] = v0[1];
+                    cz[u] = v1[0];
+                    cj[u] = (int)__double_as_longlong(v1[1]);
+                }
+#pragma unroll
+                for (int u = 0; u < 3; ++u) {
+                    if (t0 + 64 * u >= wend) break;  // uniform
+                    const int code = ccode[u];
+                    const double dx = (cx[u] - xi) + (double)shift_x(code) * g.L[0];
+                    const double dy = (cy[u] - yi) + (double)shift_y(code) * g.L[1];
+                    const double dz = (cz[u] - zi) + (double)shift_z(code) * g.L[2];
+                    const double sxy = dx * dx + dy * dy;
+                    const double r2 = sxy + dz * dz;
+                    const int j = cj[u];
+                    const bool accept = live[u] && (r2 < rc2) && !(j == i && code == zero_code);
+                    const uint64_t m = __ballot(accept);
+                    const int slot = count + __popcll(m & lt_mask);
+                    if (accept && slot < NGA_ROW_CAP) {
+                        L.r2[slot] = (uint64_t)__double_as_longlong(r2);
+                        L.j[slot] = j;
+                        L.code[slot] = code;
+                    }
+                    count += __popcll(m);
+                }
+            }
+            wave_sync_lds();  // the next window rewrites the bitmap
+        }
+        wave_sync_lds();
+        if (count > NGA_ROW_CAP) {
+            if (lane == 0) raise_bits(A.status, kBitRowCap);
+            count = 0;
+        }
+        const int keep = count < sel ? count : sel;
+        int32_t* row = A.nbr + (int64_t)i * sel;
+        int32_t* rsh = A.nbr_shift + (int64_t)i * sel * 3;
+        const double qscale = 8388608.0 / rc2;
+        if (count <= 64) sort_and_write<1>(L, count, keep, sel, qscale, row, rsh, lane);
+        else if (count <= 128) sort_and_write<2>(L, count, keep, sel, qscale, row, rsh, lane);
+        else if (count <= 256) sort_and_write<4>(L, count, keep, sel, qscale, row, rsh, lane);
+        else sort_and_write<8>(L, count, keep, sel, qscale, row, rsh, lane);
+        if (lane == 0) A.nnei[i] = keep;
+        wave_sync_lds();
+    }
+}
+
 // Work-groups per cell for select: about four centres per wavefront, which amortises each
 // work-group's stencil set-up, unless that leaves fewer than kMinSelectGroups work-groups in
 // all; then more, down to one centre per wavefront.
@@ -791,6 +1015,13 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     A.table = nullptr;
     A.cell_ptr = nullptr;
     A.n_structs = 1;
+    if (g.trim > 0) {
+        const dim3 grid((unsigned)((n + kTrimCentresPerGroup - 1) / kTrimCentresPerGroup));
+        const unsigned lds = (unsigned)(kNlWaves * sizeof(TrimList));
+        if (g.trim == 1) hipLaunchKernelGGL(select_trim_kernel<1>, grid, dim3(kNlBlock), lds, s, A);
+        else hipLaunchKernelGGL(select_trim_kernel<2>, grid, dim3(kNlBlock), lds, s, A);
+        return last_launch_status();
+    }
     const bool flat = short_segments(n, g);
     if (flat)
         hipLaunchKernelGGL((select_kernel<false, true>), dim3((unsigned)g.ncells,
@@ -1139,7 +1370,7 @@ extern "C" int nl_max_displacement(const double* pos, const double* pos_ref, int
 
 extern "C" size_t nl_build_workspace_bytes(int64_t n_atoms, const double* h_box, double rcut) {
     nga::Geom g;
-    if (!nga::make_geom(n_atoms, h_box, rcut, &g)) return 0;
+    if (!nga::make_geom(n_atoms, h_box, rcut, &g, true)) return 0;
     return nga::carve(nullptr, n_atoms, g).bytes;
 }
 
@@ -1147,7 +1378,7 @@ extern "C" int nl_build(const double* pos, int64_t n_atoms, const double* h_box,
                         int32_t sel, int32_t* nbr, int32_t* nbr_shift, int32_t* nnei, void* ws,
                         size_t ws_bytes, void* stream) {
     nga::Geom g;
-    if (!nga::make_geom(n_atoms, h_box, rcut, &g)) return NGA_EINVAL;
+    if (!nga::make_geom(n_atoms, h_box, rcut, &g, true)) return NGA_EINVAL;
     if (sel < 1) return NGA_EINVAL;
     if (n_atoms == 0) return NGA_OK;
     if (!pos || !nbr || !nbr_shift || !nnei) return NGA_EINVAL;
@@ -1195,7 +1426,7 @@ extern "C" int nl_build_static(const double* pos, int64_t n_atoms, const double*
                                double rcut, int32_t sel, int32_t* nbr, int32_t* nbr_shift,
                                int32_t* nnei, void* status, void* stream) {
     nga::Geom g;
-    if (!nga::make_geom(n_atoms, h_box, rcut, &g)) return NGA_EINVAL;
+    if (!nga::make_geom(n_atoms, h_box, rcut, &g, true)) return NGA_EINVAL;
     if (sel < 1) return NGA_EINVAL;
     if (nga::carve(nullptr, n_atoms, g).bytes > (size_t)NGA_STATIC_SCRATCH_BYTES)
         return NGA_ETOOBIG;
