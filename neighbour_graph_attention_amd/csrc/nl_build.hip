@@ -756,6 +756,17 @@ select_kernel(SelectArgs A) {
     }
 }
 
+__device__ inline int wave_excl_scan(int v, int lane, int* total) {
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    *total = __builtin_amdgcn_readlane(incl, 63);
+    return incl - v;
+}
+
 // Selection with per-centre stencils (Geom::trim = K, cells of about rcut / 2): a wavefront
 // takes one centre at a time.  Lane r < (2K+1)^2 takes stencil row (dy, dz) = (r % (2K+1) - K,
 // r / (2K+1) - K): from the centre's offset inside its own cell it finds the y and z gaps to
@@ -783,18 +794,7 @@ __device__ inline double cell_gap(int d, double f) {
     return d > 0 ? (double)d - f : (d < 0 ? f + (double)(-d - 1) : 0.0);
 }
 
-__device__ inline int wave_excl_scan(int v, int lane, int* total) {
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
-    *total = __shfl(incl, 63, 64);
-    return incl - v;
-}
-
-template <int K>
+template <int K, bool SMALL>
 __global__ void __launch_bounds__(kNlBlock) select_trim_kernel(SelectArgs A) {
     constexpr int W = 2 * K + 1, R = W * W;
     static_assert(R <= 25, "reach");
@@ -843,8 +843,10 @@ __global__ void __launch_bounds__(kNlBlock) select_trim_kernel(SelectArgs A) {
                     if (gp * gp < rem) hi = d;
                     if (gm * gm < rem) lo = -d;
                 }
+                // the stencil spans fewer cells than the box (nc >= 2K+1): one wrap at most
                 const int ry = cc[1] + dy, rz = cc[2] + dz;
-                const int ny = floor_div(ry, ncy), nz = floor_div(rz, ncz);
+                const int ny = ry < 0 ? -1 : (ry >= ncy ? 1 : 0);
+                const int nz = rz < 0 ? -1 : (rz >= ncz ? 1 : 0);
                 const int rowc = ((rz - nz * ncz) * ncy + (ry - ny * ncy)) * ncx;
                 int a0 = cc[0] + lo, a1 = cc[0] + hi, b0 = 0, b1 = -1, nxb = 0;
                 if (a0 < 0) {
@@ -865,6 +867,7 @@ __global__ void __launch_bounds__(kNlBlock) select_trim_kernel(SelectArgs A) {
         int nseg_all, total;
         const int sid = wave_excl_scan((lA > 0) + (lB > 0), lane, &nseg_all);
         const int base = wave_excl_scan(lA + lB, lane, &total);
+        total = __builtin_amdgcn_readfirstlane(total);  // alike in all lanes
         if (lA > 0) T.seg[sid] = make_int2(sA - base, cdA);
         if (lB > 0) T.seg[sid + (lA > 0)] = make_int2(sB - (base + lA), cdB);
         int count = 0;
@@ -943,9 +946,10 @@ __global__ void __launch_bounds__(kNlBlock) select_trim_kernel(SelectArgs A) {
         int32_t* row = A.nbr + (int64_t)i * sel;
         int32_t* rsh = A.nbr_shift + (int64_t)i * sel * 3;
         const double qscale = 8388608.0 / rc2;
-        if (count <= 64) sort_and_write<1>(L, count, keep, sel, qscale, row, rsh, lane);
-        else if (count <= 128) sort_and_write<2>(L, count, keep, sel, qscale, row, rsh, lane);
-        else if (count <= 256) sort_and_write<4>(L, count, keep, sel, qscale, row, rsh, lane);
+        // two sort widths only: every instance inlined here costs registers in the whole
+        // kernel.  SMALL: for rows of a few dozen candidates.
+        if (SMALL && count <= 64) sort_and_write<1>(L, count, keep, sel, qscale, row, rsh, lane);
+        else if (!SMALL && count <= 256) sort_and_write<4>(L, count, keep, sel, qscale, row, rsh, lane);
         else sort_and_write<8>(L, count, keep, sel, qscale, row, rsh, lane);
         if (lane == 0) A.nnei[i] = keep;
         wave_sync_lds();
@@ -1018,8 +1022,18 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
     if (g.trim > 0) {
         const dim3 grid((unsigned)((n + kTrimCentresPerGroup - 1) / kTrimCentresPerGroup));
         const unsigned lds = (unsigned)(kNlWaves * sizeof(TrimList));
-        if (g.trim == 1) hipLaunchKernelGGL(select_trim_kernel<1>, grid, dim3(kNlBlock), lds, s, A);
-        else hipLaunchKernelGGL(select_trim_kernel<2>, grid, dim3(kNlBlock), lds, s, A);
+        // neighbours within rcut at the mean density
+        const double vol = g.L[0] * g.L[1] * g.L[2];
+        const double expect = (double)n / vol * 4.18879020478639 * rcut * rcut * rcut;
+        const bool small = expect <= 48.0;
+        if (g.trim == 1 && small)
+            hipLaunchKernelGGL((select_trim_kernel<1, true>), grid, dim3(kNlBlock), lds, s, A);
+        else if (g.trim == 1)
+            hipLaunchKernelGGL((select_trim_kernel<1, false>), grid, dim3(kNlBlock), lds, s, A);
+        else if (small)
+            hipLaunchKernelGGL((select_trim_kernel<2, true>), grid, dim3(kNlBlock), lds, s, A);
+        else
+            hipLaunchKernelGGL((select_trim_kernel<2, false>), grid, dim3(kNlBlock), lds, s, A);
         return last_launch_status();
     }
     const bool flat = short_segments(n, g);
