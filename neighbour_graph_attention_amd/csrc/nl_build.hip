@@ -367,8 +367,13 @@ struct WaveList {
     uint16_t pay[NGA_ROW_CAP];
 };
 
-__device__ inline uint64_t lo_key(const WaveList& L, int p) {
-    return ((uint64_t)(uint32_t)L.j[p] << 24) | (uint64_t)(uint32_t)L.code[p];
+// The list seen through an LDS pointer: where the sort is a called function rather than
+// inlined, a plain reference would leave it generic (flat) memory accesses.
+typedef __attribute__((address_space(3))) WaveList LdsList;
+__device__ inline LdsList* lds(WaveList& L) { return (LdsList*)&L; }
+
+__device__ inline uint64_t lo_key(const LdsList* L, int p) {
+    return ((uint64_t)(uint32_t)L->j[p] << 24) | (uint64_t)(uint32_t)L->code[p];
 }
 
 // Sort words: a 23-bit distance class above the 9-bit list index of the candidate.
@@ -440,8 +445,8 @@ __device__ inline void wave_sync_lds() {
 }
 
 // Full key of list entry p, compared as (r2 bit pattern, j, shift code).
-__device__ inline bool full_less(const WaveList& L, int a, int b) {
-    if (L.r2[a] != L.r2[b]) return L.r2[a] < L.r2[b];
+__device__ inline bool full_less(const LdsList* L, int a, int b) {
+    if (L->r2[a] != L->r2[b]) return L->r2[a] < L->r2[b];
     return lo_key(L, a) < lo_key(L, b);
 }
 
@@ -452,13 +457,13 @@ __device__ inline bool full_less(const WaveList& L, int a, int b) {
 // wide, so it takes r2 values within about 1e-5 A^2 of each other at rcut = 8 A, such as the
 // exact ties of ideal lattices).
 template <int NS>
-__device__ void sort_and_write(WaveList& L, int count, int keep, int sel, double qscale,
+__device__ void sort_and_write(LdsList* L, int count, int keep, int sel, double qscale,
                                int32_t* row, int32_t* rsh, int lane) {
     uint32_t k[NS];
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
         const int e = lane * NS + q;
-        k[q] = e < count ? (dist_class(L.r2[e], qscale) << kIndexBits) | (uint32_t)e : ~0u;
+        k[q] = e < count ? (dist_class(L->r2[e], qscale) << kIndexBits) | (uint32_t)e : ~0u;
     }
     bitonic_sort<NS>(k, lane);
 
@@ -479,7 +484,7 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, double
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
             const int e = lane * NS + q;
-            if (e < count) L.pay[e] = (uint16_t)(k[q] & kIndexMask);
+            if (e < count) L->pay[e] = (uint16_t)(k[q] & kIndexMask);
         }
         wave_sync_lds();
 #pragma unroll
@@ -489,11 +494,11 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, double
             const uint32_t cls = k[q] >> kIndexBits;
             const int me = (int)(k[q] & kIndexMask);
             int rs = e, re = e + 1;
-            while (rs > 0 && dist_class(L.r2[L.pay[rs - 1]], qscale) == cls) --rs;
-            while (re < count && dist_class(L.r2[L.pay[re]], qscale) == cls) ++re;
+            while (rs > 0 && dist_class(L->r2[L->pay[rs - 1]], qscale) == cls) --rs;
+            while (re < count && dist_class(L->r2[L->pay[re]], qscale) == cls) ++re;
             if (re - rs == 1) continue;
             int rank = 0;
-            for (int t = rs; t < re; ++t) rank += full_less(L, L.pay[t], me);
+            for (int t = rs; t < re; ++t) rank += full_less(L, L->pay[t], me);
             pos[q] = rs + rank;
         }
     }
@@ -505,8 +510,8 @@ __device__ void sort_and_write(WaveList& L, int count, int keep, int sel, double
             const int at = pos[q];
             if (at < keep) {
                 const int p = (int)(k[q] & kIndexMask);
-                const int code = L.code[p];
-                row[at] = L.j[p];
+                const int code = L->code[p];
+                row[at] = L->j[p];
                 rsh[3 * at + 0] = shift_x(code);
                 rsh[3 * at + 1] = shift_y(code);
                 rsh[3 * at + 2] = shift_z(code);
@@ -747,10 +752,10 @@ select_kernel(SelectArgs A) {
         int32_t* row = A.nbr + (int64_t)i * sel;
         int32_t* rsh = A.nbr_shift + (int64_t)i * sel * 3;
         const double qscale = 8388608.0 / rc2;
-        if (count <= 64) sort_and_write<1>(L, count, keep, sel, qscale, row, rsh, lane);
-        else if (count <= 128) sort_and_write<2>(L, count, keep, sel, qscale, row, rsh, lane);
-        else if (count <= 256) sort_and_write<4>(L, count, keep, sel, qscale, row, rsh, lane);
-        else sort_and_write<8>(L, count, keep, sel, qscale, row, rsh, lane);
+        if (count <= 64) sort_and_write<1>(lds(L), count, keep, sel, qscale, row, rsh, lane);
+        else if (count <= 128) sort_and_write<2>(lds(L), count, keep, sel, qscale, row, rsh, lane);
+        else if (count <= 256) sort_and_write<4>(lds(L), count, keep, sel, qscale, row, rsh, lane);
+        else sort_and_write<8>(lds(L), count, keep, sel, qscale, row, rsh, lane);
         if (lane == 0) A.nnei[i] = keep;
         wave_sync_lds();
     }
@@ -948,9 +953,9 @@ __global__ void __launch_bounds__(kNlBlock) select_trim_kernel(SelectArgs A) {
         const double qscale = 8388608.0 / rc2;
         // two sort widths only: every instance inlined here costs registers in the whole
         // kernel.  SMALL: for rows of a few dozen candidates.
-        if (SMALL && count <= 64) sort_and_write<1>(L, count, keep, sel, qscale, row, rsh, lane);
-        else if (!SMALL && count <= 256) sort_and_write<4>(L, count, keep, sel, qscale, row, rsh, lane);
-        else sort_and_write<8>(L, count, keep, sel, qscale, row, rsh, lane);
+        if (SMALL && count <= 64) sort_and_write<1>(lds(L), count, keep, sel, qscale, row, rsh, lane);
+        else if (!SMALL && count <= 256) sort_and_write<4>(lds(L), count, keep, sel, qscale, row, rsh, lane);
+        else sort_and_write<8>(lds(L), count, keep, sel, qscale, row, rsh, lane);
         if (lane == 0) A.nnei[i] = keep;
         wave_sync_lds();
     }
@@ -1269,10 +1274,10 @@ __global__ void __launch_bounds__(kNlBlock) refine_kernel(RefineArgs A) {
     int32_t* row = A.nbr + (int64_t)i * A.sel;
     int32_t* rsh = A.nbr_shift + (int64_t)i * A.sel * 3;
     const double qscale = 8388608.0 / A.rc2;
-    if (count <= 64) sort_and_write<1>(L, count, keep, A.sel, qscale, row, rsh, lane);
-    else if (count <= 128) sort_and_write<2>(L, count, keep, A.sel, qscale, row, rsh, lane);
-    else if (count <= 256) sort_and_write<4>(L, count, keep, A.sel, qscale, row, rsh, lane);
-    else sort_and_write<8>(L, count, keep, A.sel, qscale, row, rsh, lane);
+    if (count <= 64) sort_and_write<1>(lds(L), count, keep, A.sel, qscale, row, rsh, lane);
+    else if (count <= 128) sort_and_write<2>(lds(L), count, keep, A.sel, qscale, row, rsh, lane);
+    else if (count <= 256) sort_and_write<4>(lds(L), count, keep, A.sel, qscale, row, rsh, lane);
+    else sort_and_write<8>(lds(L), count, keep, A.sel, qscale, row, rsh, lane);
     if (lane == 0) A.nnei[i] = keep;
     if (__ballot(bad) && lane == 0) raise_bits(A.status, kBitIndex);
 }
