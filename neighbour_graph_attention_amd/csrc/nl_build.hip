@@ -404,7 +404,14 @@ __device__ inline uint32_t xor_lanes(uint32_t v, int lx) {
     }
 }
 
+// min(a, b) when c = 0, max(a, b) when c = ~0: the median of the three, one v_med3_u32.
+__device__ inline uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+    return min(max(a, b), max(min(a, b), c));
+}
+
 // Bitonic sort of 64*NS 32-bit words held NS per lane (element e = lane*NS + q), ascending.
+// Every compare-exchange is one median-of-three against a per-stage mask word that says
+// whether this position keeps the smaller or the larger word.
 template <int NS>
 __device__ inline void bitonic_sort(uint32_t (&k)[NS], int lane) {
     constexpr int M = 64 * NS;
@@ -417,22 +424,21 @@ __device__ inline void bitonic_sort(uint32_t (&k)[NS], int lane) {
                 for (int q = 0; q < NS; ++q) {
                     if (q & stride) continue;
                     const int o = q | stride;
-                    const int e = lane * NS + q;
-                    const bool ascending = (e & size) == 0;
-                    const uint32_t lo = min(k[q], k[o]), hi = max(k[q], k[o]);
-                    k[q] = ascending ? lo : hi;
-                    k[o] = ascending ? hi : lo;
+                    // e & size: from q alone below NS, from the lane above
+                    const bool ascending = size < NS ? (q & size) == 0 : ((lane * NS) & size) == 0;
+                    const uint32_t keep = ascending ? 0u : ~0u;
+                    const uint32_t a = k[q], b = k[o];
+                    k[q] = med3u(a, b, keep);
+                    k[o] = med3u(a, b, ~keep);
                 }
             } else {
                 const int lx = stride / NS;
+                // e & size and e & stride come from the lane (size > stride >= NS)
+                const bool ascending = ((lane * NS) & size) == 0;
+                const bool lower = ((lane * NS) & stride) == 0;
+                const uint32_t keep = lower == ascending ? 0u : ~0u;
 #pragma unroll
-                for (int q = 0; q < NS; ++q) {
-                    const int e = lane * NS + q;
-                    const uint32_t ok = xor_lanes(k[q], lx);
-                    const bool ascending = (e & size) == 0;
-                    const bool lower = (e & stride) == 0;
-                    k[q] = lower == ascending ? min(ok, k[q]) : max(ok, k[q]);
-                }
+                for (int q = 0; q < NS; ++q) k[q] = med3u(xor_lanes(k[q], lx), k[q], keep);
             }
         }
     }
