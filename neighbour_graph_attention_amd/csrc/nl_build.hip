@@ -767,13 +767,19 @@ select_kernel(SelectArgs A) {
     }
 }
 
+// Exclusive prefix sum over the wavefront (and the total), with DPP moves only: shifts by 1,
+// 2, 4 and 8 inside each row of 16 lanes (zero shifted in), then each row's running total
+// broadcast into the next rows (row_bcast 15 into rows 1 and 3, row_bcast 31 into rows 2 and
+// 3).
 __device__ inline int wave_excl_scan(int v, int lane, int* total) {
+    (void)lane;
     int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-    }
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, true);  // row_shr:1
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, true);  // row_shr:2
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, true);  // row_shr:4
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, true);  // row_shr:8
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xC, 0xF, false);  // row_bcast:31
     *total = __builtin_amdgcn_readlane(incl, 63);
     return incl - v;
 }
@@ -929,9 +935,11 @@ __global__ void __launch_bounds__(kNlBlock) select_trim_kernel(SelectArgs A) {
                 for (int u = 0; u < 3; ++u) {
                     if (t0 + 64 * u >= wend) break;  // uniform
                     const int code = ccode[u];
-                    const double dx = (cx[u] - xi) + (double)shift_x(code) * g.L[0];
-                    const double dy = (cy[u] - yi) + (double)shift_y(code) * g.L[1];
-                    const double dz = (cz[u] - zi) + (double)shift_z(code) * g.L[2];
+                    // n L is exact for n in {-1, 0, 1}, so the fused form rounds once, as
+                    // the pinned (x_j - x_i) + n L does
+                    const double dx = __builtin_fma((double)shift_x(code), g.L[0], cx[u] - xi);
+                    const double dy = __builtin_fma((double)shift_y(code), g.L[1], cy[u] - yi);
+                    const double dz = __builtin_fma((double)shift_z(code), g.L[2], cz[u] - zi);
                     const double sxy = dx * dx + dy * dy;
                     const double r2 = sxy + dz * dz;
                     const int j = cj[u];
