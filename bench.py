@@ -119,6 +119,22 @@ def load_traffic(variant: str, workload: str):
     return float(doc["hbm_bytes_per_launch"])
 
 
+NL_SOURCES = ["neighbour_graph_attention_amd/csrc/nl_build.hip",
+              "neighbour_graph_attention_amd/csrc/scan.hip"]
+
+
+def load_nl_traffic(workload: str):
+    """Measured HBM bytes of one nl_build call (all its kernels), if the committed counter
+    summary was taken on the current source; else None."""
+    path = os.path.join(ROOT, "profiles", f"nl_build.{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    doc = json.load(open(path))
+    if doc.get("source_sha256") != source_digest(NL_SOURCES):
+        return None
+    return float(doc["hbm_bytes_per_call"])
+
+
 def cpu_baseline(w, pos, box, rp, x, wt, target_s):
     """The oracle (brute-force rows + naive attention through every layer) on sampled centres."""
     import oracle
@@ -538,6 +554,7 @@ def main():
     peak_basis = f"{w.dtype} dense MFMA"
     traffic = load_traffic(variant, w.name)
     nl_bytes = 24.0 * n + 8.0 * (n + 1) + 16.0 * e
+    nl_counter = load_nl_traffic(w.name)
     nl_gbs = nl_bytes / ((nl_ms + csr_ms) * 1e-3) / 1e9
     # edge_csr alone: read each kept row entry (j, 3 shifts) and nnei, write col, shift, dst
     # and row_ptr.
@@ -567,7 +584,11 @@ def main():
         "parts_ms": {"nl_build": nl_ms, "edge_csr": csr_ms, "block_attn_forward": attn_ms},
         "timing": timing,
         "nl_hbm": {"algorithmic_bytes": nl_bytes, "achieved_gbs": nl_gbs,
-                   "frac": nl_gbs / PEAK_HBM_GBS},
+                   "frac": nl_gbs / PEAK_HBM_GBS,
+                   # nl_build's own HBM bytes from the committed FETCH_SIZE / WRITE_SIZE
+                   # summary, over nl_build's time alone
+                   "counter_bytes": nl_counter,
+                   "counter_gbs": None if nl_counter is None else nl_counter / (nl_ms * 1e-3) / 1e9},
         "csr_hbm": {"algorithmic_bytes": csr_bytes, "achieved_gbs": csr_gbs,
                     "frac": csr_gbs / PEAK_HBM_GBS},
     }
