@@ -25,6 +25,7 @@
 #include "gemm_rows.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace nga {
 
@@ -604,6 +605,213 @@ int local_chunk_rows(int c, int heads, size_t es) {
 
 // Work-groups of a persistent kernel: as many as the current device holds at once (resident
 // work-groups per compute unit for this kernel, from its registers and LDS, times the units).
+// fp32, four heads of c = 64 channels: the streaming pass on the matrix cores, one wavefront
+// per centre at a time (wavefront w of the grid takes centres w, w + W, ...; no work-group
+// barriers), in blocks of 16 rows.  v_mfma_f32_4x4x1_16b_f32 forms 16 independent 4x4 outer
+// products per instruction; block b of it takes A[i] from lane 4b + i and B[j] from lane
+// 4b + j and accumulates D[i][j] in lane 4b + j, register i.
+//   scores  block b = (row group b % 4, channel slice b / 4): lane L holds row L % 16 of the
+//           16-row block and channels 16u + 4 (L / 16) + e (u, e < 4) of it, straight from its
+//           16-byte global loads, against R of head L % 4 for the same channels (registers,
+//           per centre); 16 products, then the four slices summed across lanes (xor 16, 32).
+//           Lane L then owns the score of row 4 ((L / 4) % 4) + L / 16 for head L % 4.
+//   weights exp2(s - m_h) with the lazily moved shift of local_stream_h4_kernel, per wavefront.
+//   sums    block b = columns 4b .. 4b + 3: per row, A[i] = the row's weight for head i, B[j] =
+//           the row's column 4b + j (a transposed copy of the block in the wavefront's LDS), so
+//           lane L accumulates U_h[L] for the four heads in its four D registers.
+#ifndef NGA_LOCAL_MFMA
+#define NGA_LOCAL_MFMA 1
+#endif
+constexpr bool kLocalMfma = NGA_LOCAL_MFMA;
+constexpr int kMfRows = 16;
+#ifndef NGA_LOCAL_AHEAD
+#define NGA_LOCAL_AHEAD 1
+#endif
+constexpr int kMfAhead = NGA_LOCAL_AHEAD;  // blocks whose loads are in flight
+constexpr int kMfLd = 64 + 4;  // padded LDS row, floats
+
+// LDS writes of this wavefront visible to its own later reads (no work-group barrier).
+__device__ inline void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool ORD>
+__global__ void __launch_bounds__(kLocalThreads) local_mfma_kernel(LocalArgs<float> A) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    constexpr int C = 64, H = 4, RB = kMfRows;
+    __shared__ __align__(16) float sXw[kLocalThreads / 64][RB * kMfLd];
+    __shared__ __align__(16) float sPw[kLocalThreads / 64][H * RB];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float* sX = sXw[wave];
+    float* sPT = sPw[wave];
+    const int G = lane >> 4, r16 = lane & 15, hq = lane & 3;
+    const int own_row = 4 * ((lane >> 2) & 3) + G;  // the row this lane's score belongs to
+    const int64_t N = A.n_centres;
+    const int64_t W = (int64_t)gridDim.x * (kLocalThreads / 64);
+    bool bad_index = false;
+
+    // the first non-empty centre at or after i on this wavefront's stride; empty ones get zeros
+    auto first_block = [&](int64_t i) -> LocalTask {
+        for (; i < N; i += W) {
+            const int64_t r0 = uniform64(A.row_ptr[i]), r1 = uniform64(A.row_ptr[i + 1]);
+            if (r0 < 0 || r1 < r0 || r1 > A.n_edges) {
+                if (lane == 0) raise_bits(A.status, kBitCap);
+                continue;
+            }
+            if (r1 > r0) return LocalTask{i, r0, r1 - r0, 0};
+            float* un = A.un + i * (H * C);
+#pragma unroll
+            for (int h = 0; h < H; ++h) un[h * C + lane] = 0.f;
+        }
+        return LocalTask{N, 0, 0, 0};
+    };
+    auto next_block = [&](const LocalTask& t) -> LocalTask {
+        if (t.j0 + RB < t.n) return LocalTask{t.i, t.r0, t.n, t.j0 + RB};
+        return first_block(t.i + W);
+    };
+    // Blocks in flight ahead of the current one: lane L loads the 16-byte vectors 4u + L / 16 of
+    // row L % 16 (the score operands as they stand); rows past the centre's end repeat its
+    // last row (weight 0).
+    f4 xa[4], xn[4], xm[4];
+    auto fetch = [&](f4 (&dst)[4], const LocalTask& t) {
+        const int rows = (int)(t.n - t.j0 < RB ? t.n - t.j0 : RB);
+        const int j = r16 < rows - 1 ? r16 : rows - 1;
+        int64_t row = t.r0 + t.j0 + j;
+        if (ORD) {
+            row = A.order[row];
+            if (row < 0 || row >= A.n_edges) {
+                bad_index = true;
+                row = 0;
+            }
+        }
+        const f4* xr = reinterpret_cast<const f4*>(A.x + row * C);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dst[u] = xr[4 * u + G];
+    };
+
+    LocalTask cur = first_block((int64_t)blockIdx.x * (kLocalThreads / 64) + wave);
+    // two ahead: nxt is the block after cur, its loads issued already
+    LocalTask nxt = (kMfAhead == 2 && cur.i < N) ? next_block(cur) : cur;
+    if (cur.i < N) fetch(xa, cur);
+    if (kMfAhead == 2 && nxt.i < N) fetch(xn, nxt);
+    f4 rr[4];                          // R of head hq, channels 16u + 4G .. + 3, in base-2 units
+    f4 U0 = {0.f, 0.f, 0.f, 0.f}, U1 = U0;  // U_h[lane] over even / odd rows
+    float m = 0.f, zl = 0.f;           // head hq's shift; this lane's part of Z_hq
+    while (cur.i < N) {
+        LocalTask nn;  // the block whose loads are issued now
+        if (kMfAhead == 2) {
+            nn = nxt.i < N ? next_block(nxt) : nxt;
+            if (nn.i < N) fetch(xm, nn);
+        } else {
+            nn = next_block(cur);
+            if (nn.i < N) fetch(xn, nn);
+        }
+        const bool fresh = cur.j0 == 0;
+        if (fresh) {
+            const f4* rp = reinterpret_cast<const f4*>(A.r + cur.i * (H * C) + hq * C);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) rr[u] = rp[4 * u + G] * Base2<float>::scale;
+        }
+        const int rows = (int)(cur.n - cur.j0 < RB ? cur.n - cur.j0 : RB);
+        // scores: 16 products in two chains, then the four channel slices summed
+        f4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = d0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            d0 = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[u][0], rr[u][0], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[u][1], rr[u][1], d1, 0, 0, 0);
+            d0 = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[u][2], rr[u][2], d0, 0, 0, 0);
+            d1 = __builtin_amdgcn_mfma_f32_4x4x1f32(xa[u][3], rr[u][3], d1, 0, 0, 0);
+        }
+        f4 d = d0 + d1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            d[e] += __shfl_xor(d[e], 16, 64);
+            d[e] += __shfl_xor(d[e], 32, 64);
+        }
+        const float sv = G == 0 ? d[0] : (G == 1 ? d[1] : (G == 2 ? d[2] : d[3]));
+        const bool valid = own_row < rows;
+        // the shift: 0 at a centre's start, moved only when a score passes it by more than
+        // `lead`, or when a centre's first block has no score within `lead` below it
+        const bool over = valid && sv > m + Base2<float>::lead;
+        const bool near = valid && sv >= m - Base2<float>::lead;
+        // lanes L with L % 4 = h hold head h: a head with no score near its shift in a centre's
+        // first block has its shift lowered (every head has row 0 there)
+        const uint64_t nm = __ballot(near);
+        const bool some_head_far = (nm & 0x1111111111111111ull) == 0 || (nm & 0x2222222222222222ull) == 0 ||
+                                   (nm & 0x4444444444444444ull) == 0 || (nm & 0x8888888888888888ull) == 0;
+        if (__any(over) || (fresh && some_head_far)) {
+            float mc = valid ? sv : -INFINITY;
+#pragma unroll
+            for (int off = 4; off < 64; off <<= 1) {
+                const float o = __shfl_xor(mc, off, 64);
+                mc = o > mc ? o : mc;
+            }
+            const float mnew = fresh ? mc : (mc > m ? mc : m);
+            const float alpha = fresh ? 1.f : Base2<float>::ex(m - mnew);
+            zl *= alpha;
+            m = mnew;
+            f4 al;
+#pragma unroll
+            for (int h = 0; h < H; ++h) al[h] = __shfl(alpha, h, 64);  // lane h holds head h
+            U0 *= al;
+            U1 *= al;
+        }
+        const float p = valid ? Base2<float>::ex(sv - m) : 0.f;
+        zl += p;
+        // the block and its weights into this wavefront's LDS, transposed for the sums
+        sPT[hq * RB + own_row] = p;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) *reinterpret_cast<f4*>(&sX[r16 * kMfLd + 16 * u + 4 * G]) = xa[u];
+        wave_sync_lds();
+        f4 pa[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pa[q] = *reinterpret_cast<const f4*>(&sPT[hq * RB + 4 * q]);
+#pragma unroll
+        for (int r = 0; r < RB; r += 2) {
+            U0 = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[r / 4][r % 4], sX[r * kMfLd + lane], U0, 0, 0, 0);
+            U1 = __builtin_amdgcn_mfma_f32_4x4x1f32(pa[r / 4][r % 4 + 1], sX[(r + 1) * kMfLd + lane], U1, 0, 0, 0);
+        }
+        wave_sync_lds();  // the next block rewrites the buffers
+        if (cur.j0 + RB >= cur.n) {
+            // the centre's end: Z_h from the lanes' parts (lanes with equal hq), U_h / Z_h
+            float z = zl;
+#pragma unroll
+            for (int off = 4; off < 64; off <<= 1) z += __shfl_xor(z, off, 64);
+            const f4 U = U0 + U1;
+            float* un = A.un + cur.i * (H * C);
+#pragma unroll
+            for (int h = 0; h < H; ++h) un[h * C + lane] = U[h] * (1.f / __shfl(z, h, 64));
+            U0 = f4{0.f, 0.f, 0.f, 0.f};
+            U1 = U0;
+            m = 0.f;
+            zl = 0.f;
+        }
+        if (kMfAhead == 2) {
+            cur = nxt;
+            nxt = nn;
+        } else {
+            cur = nn;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            xa[u] = xn[u];
+            if (kMfAhead == 2) xn[u] = xm[u];
+        }
+    }
+    if (bad_index) raise_bits(A.status, kBitIndex);
+}
+
+template <bool ORD>
+void launch_mfma_o(const LocalArgs<float>& a, hipStream_t s) {
+    const void* k = reinterpret_cast<const void*>(&local_mfma_kernel<ORD>);
+    // one wavefront per centre at most
+    const int64_t groups = std::min<int64_t>((a.n_centres + 3) / 4, resident_groups(k, kLocalThreads));
+    hipLaunchKernelGGL((local_mfma_kernel<ORD>), dim3((unsigned)(groups < 1 ? 1 : groups)),
+                       dim3(kLocalThreads), 0, s, a);
+}
+
 template <typename T, int CV, bool ORD>
 void launch_stream_h4_o(const LocalArgs<T>& a, hipStream_t s) {
     const void* k = reinterpret_cast<const void*>(&local_stream_h4_kernel<T, CV, ORD>);
@@ -676,7 +884,10 @@ int run_local(const int64_t* row_ptr, const int32_t* order, int64_t n_centres, i
         const int nv = hc / Vec<T>::n;
         const int loads = (chunk * (c / Vec<T>::n) + kLocalThreads - 1) / kLocalThreads;
         const int cvec = c / Vec<T>::n;
-        if (heads == 4 && (cvec == 4 || cvec == 8 || cvec == 16)) {
+        if (std::is_same<T, float>::value && heads == 4 && c == 64 && kLocalMfma) {
+            if (order) launch_mfma_o<true>(reinterpret_cast<const LocalArgs<float>&>(a), s);
+            else launch_mfma_o<false>(reinterpret_cast<const LocalArgs<float>&>(a), s);
+        } else if (heads == 4 && (cvec == 4 || cvec == 8 || cvec == 16)) {
             if (cvec == 4) launch_stream_h4<T, 4>(a, s);
             else if (cvec == 8) launch_stream_h4<T, 8>(a, s);
             else launch_stream_h4<T, 16>(a, s);

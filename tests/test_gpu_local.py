@@ -94,6 +94,7 @@ CASES = [
     (np.float64, 40, 130, 128, 4, 2, 6),     # 55 rows per chunk
     (np.float64, 30, 70, 32, 4, 6, 7),
     (np.float64, 20, 200, 20, 2, 1, 8),
+    (np.float32, 30, 150, 32, 4, 2, 10),
 ]
 
 
@@ -101,7 +102,8 @@ CASES = [
 def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, seed):
     rp = W.random_rows(nc, maxlen, seed)
     lens = np.diff(rp)
-    for k, v in enumerate([0, 1, maxlen, 63, 64, 65, 128, 129]):
+    # empty, one row, the cap, and the edges of 16-row blocks and 64-row chunks
+    for k, v in enumerate([0, 1, maxlen, 63, 64, 65, 128, 129, 15, 16, 17, 31, 33]):
         lens[k] = min(v, maxlen)
     rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
     e = int(rp[-1])
@@ -165,24 +167,29 @@ def test_large_scores_move_the_shift(oracle_mod, dtype, amp):
     assert err < TOL[dtype]
 
 
-def test_order_gather(oracle_mod):
+@pytest.mark.parametrize("dtype,c", [(np.float64, 32), (np.float32, 64), (np.float32, 32)])
+def test_order_gather(oracle_mod, dtype, c):
     rp = W.random_rows(30, 90, 77, min_len=1)
     e = int(rp[-1])
-    x = W.make_features(e, 32, 78, np.float64)
-    xc = W.make_features(30, 32, 79, np.float64)
-    wt = W.make_weights(2, 32, 80, np.float64)
+    x = W.make_features(e, c, 78, np.float64)
+    xc = W.make_features(30, c, 79, np.float64)
+    wt = W.make_weights(2, c, 80, np.float64)
     perm = np.random.default_rng(81).permutation(e).astype(np.int32)
     x2 = np.empty_like(x)
     x2[perm] = x
-    y = _local(rp, xc, x2, wt, 4, order=perm)
-    assert _normwise(y, oracle_mod.local_atten(rp, xc, x, wt, 4)) < TOL[np.float64]
+    y = _local(rp, xc.astype(dtype), x2.astype(dtype), wt.astype(dtype), 4, order=perm)
+    ref = oracle_mod.local_atten(rp, xc.astype(dtype).astype(np.float64),
+                                 x.astype(dtype).astype(np.float64),
+                                 wt.astype(dtype).astype(np.float64), 4)
+    assert _normwise(y.astype(np.float64), ref) < TOL[dtype]
 
 
-def test_order_out_of_range_is_reported():
+@pytest.mark.parametrize("c", [16, 64])
+def test_order_out_of_range_is_reported(c):
     rp = np.array([0, 4, 8], np.int64)
-    x = W.make_features(8, 16, 1, np.float32)
-    xc = W.make_features(2, 16, 2, np.float32)
-    wt = W.make_weights(1, 16, 3, np.float32)
+    x = W.make_features(8, c, 1, np.float32)
+    xc = W.make_features(2, c, 2, np.float32)
+    wt = W.make_weights(1, c, 3, np.float32)
     t = lambda a: torch.from_numpy(a).to(DEV)
     order = torch.tensor([0, 1, 2, 3, 4, 5, 6, 99], dtype=torch.int32, device=DEV)
     ws = nga.Workspace(DEV)
@@ -190,11 +197,12 @@ def test_order_out_of_range_is_reported():
     assert nga.sync_status(ws) == -8
 
 
-def test_bad_row_ptr_is_reported():
+@pytest.mark.parametrize("c", [16, 64])
+def test_bad_row_ptr_is_reported(c):
     rp = np.array([0, 4, 20], np.int64)  # beyond the 8 edge rows
-    x = W.make_features(8, 16, 1, np.float32)
-    xc = W.make_features(2, 16, 2, np.float32)
-    wt = W.make_weights(1, 16, 3, np.float32)
+    x = W.make_features(8, c, 1, np.float32)
+    xc = W.make_features(2, c, 2, np.float32)
+    wt = W.make_weights(1, c, 3, np.float32)
     t = lambda a: torch.from_numpy(a).to(DEV)
     ws = nga.Workspace(DEV)
     nga.local_attn_forward(t(rp), t(xc), t(x), t(wt), 4, ws=ws)
