@@ -104,6 +104,9 @@ def test_ideal_lattices_bitexact(oracle_mod, lattice, ncells, a, rcut, sel):
     (8193, (60.0, 60.0, 60.0), 3.7, 24, 9),   # one atom past them: multi-launch binning
     (3000, (20.0, 20.0, 20.0), 5.0, 60, 10),  # ~47 atoms per cell: per-segment candidate rounds
     (1500, (20.0, 20.0, 20.0), 5.0, 60, 11),  # ~23 atoms per cell: rounds across segment ends
+    # dense, five half-size cells per axis: ~1,100 candidates per centre, more than one
+    # 1,024-position window of the per-centre stencil's run bitmap; ~390 neighbours, rows cut
+    (2400, (11.8, 11.8, 11.8), 4.0, 300, 12),
 ])
 def test_random_boxes_bitexact(oracle_mod, n, box, rcut, sel, seed):
     pos = W.random_positions(n, box, seed)
