@@ -53,15 +53,15 @@ __device__ inline void raise_bits(uint32_t* status, uint32_t bits) { atomicOr(st
 
 inline bool finite_pos(double v) { return std::isfinite(v) && v > 0.0; }
 
-// Tiled exclusive scan of int32 counts into int64 offsets (scan.hip).
-// out[0] = 0, out[i+1] = sum(counts[0..i]); tile_sums holds scan_tiles(n) int64.
+// Exclusive scan of clamped int32 counts into int64 offsets (scan.hip):
+// out[0] = 0, out[i+1] = sum over j <= i of min(max(counts[j], 0), hi).  tile_sums is
+// scratch of scan_tiles(n) int64 (used only for long inputs).
 constexpr int kScanBlock = 256;
 constexpr int kScanItems = 8;
 constexpr int kScanTile = kScanBlock * kScanItems;
 inline int64_t scan_tiles(int64_t n) { return (n + kScanTile - 1) / kScanTile; }
-int scan_counts_tile_sums(const int32_t* counts, int64_t n, int64_t* tile_sums, hipStream_t s);
-int scan_counts_finish(const int32_t* counts, int64_t n, const int64_t* tile_sums, int64_t* out,
-                       hipStream_t s);
+int scan_counts(const int32_t* counts, int64_t n, int32_t hi, int64_t* tile_sums, int64_t* out,
+                hipStream_t s);
 
 // Status word handling (edge_csr.hip).
 int status_from_bits(uint32_t bits);

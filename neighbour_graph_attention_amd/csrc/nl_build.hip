@@ -1017,8 +1017,7 @@ int launch_nl(const double* pos, int64_t n, const Geom& g, double rcut, int32_t 
         hipLaunchKernelGGL(bin_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni, g,
                            w.cell_count, w.atom_cell, w.atom_slot, status);
         if ((rc = last_launch_status())) return rc;
-        if ((rc = scan_counts_tile_sums(w.cell_count, g.ncells, w.tile_sums, s))) return rc;
-        if ((rc = scan_counts_finish(w.cell_count, g.ncells, w.tile_sums, w.cell_start, s)))
+        if ((rc = scan_counts(w.cell_count, g.ncells, INT32_MAX, w.tile_sums, w.cell_start, s)))
             return rc;
         hipLaunchKernelGGL(scatter_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,
                            w.cell_start, w.atom_cell, w.atom_slot, w.sa);
@@ -1157,8 +1156,7 @@ int launch_nl_batch(const double* pos, const BatchPlan& p, double rcut, int32_t 
                            b.table, b.atom_ptr, ns, w.cell_count, w.atom_cell, w.atom_slot,
                            status);
     if ((rc = last_launch_status())) return rc;
-    if ((rc = scan_counts_tile_sums(w.cell_count, p.n_cells, w.tile_sums, s))) return rc;
-    if ((rc = scan_counts_finish(w.cell_count, p.n_cells, w.tile_sums, w.cell_start, s)))
+    if ((rc = scan_counts(w.cell_count, p.n_cells, INT32_MAX, w.tile_sums, w.cell_start, s)))
         return rc;
     if (ni == 0) return NGA_OK;
     hipLaunchKernelGGL(scatter_kernel, dim3((ni + 255) / 256), dim3(256), 0, s, pos, ni,

@@ -216,8 +216,7 @@ int run_pair(const int64_t* row_ptr, const int32_t* order, const std::vector<Chu
     hipLaunchKernelGGL(pair_counts_kernel, pair_grid(n_centres), dim3(kPairBlock), 0, s, row_ptr,
                        n_centres, w.counts);
     if ((rc = last_launch_status())) return rc;
-    if ((rc = scan_counts_tile_sums(w.counts, n_centres, w.tile_sums, s))) return rc;
-    if ((rc = scan_counts_finish(w.counts, n_centres, w.tile_sums, w.pair_ptr, s))) return rc;
+    if ((rc = scan_counts(w.counts, n_centres, INT32_MAX, w.tile_sums, w.pair_ptr, s))) return rc;
 
     T* qkv = static_cast<T*>(w.qkv);
     T* o = static_cast<T*>(w.o);

@@ -189,6 +189,42 @@ def test_edge_mask_compaction_keeps_slot_order():
     assert np.array_equal(csr["dst"].cpu().numpy(), np.nonzero(mask)[0])
 
 
+@pytest.mark.parametrize("n", [1, 8191, 8192, 8193, 40000, 65536, 65537, 100003])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_row_counts_clamped_and_scanned(n, offset):
+    """row_ptr is the running sum of nnei clamped to [0, sel], and each row keeps its first
+    slots, at sizes on both sides of every scan tile and launch-shape boundary; offset 1
+    hands nnei in at an address that is not 16-byte aligned."""
+    rng = np.random.default_rng(n + offset)
+    sel = 4
+    nbr = rng.integers(0, n, size=(n, sel)).astype(np.int32)
+    sh = rng.integers(-1, 2, size=(n, sel, 3)).astype(np.int32)
+    nnei = rng.integers(-3, sel + 4, size=n + offset).astype(np.int32)
+    buf = torch.from_numpy(nnei).to(DEV)
+    print(f"n={n} offset={offset}", flush=True)
+    csr = nga.edge_csr(torch.from_numpy(nbr).to(DEV), torch.from_numpy(sh).to(DEV), buf[offset:])
+    nga.check_status(csr["ws"], "clamped csr")
+    cnt = np.clip(nnei[offset:], 0, sel)
+    assert np.array_equal(csr["row_ptr"].cpu().numpy(), np.concatenate([[0], np.cumsum(cnt)]))
+    keep = np.arange(sel)[None, :] < cnt[:, None]
+    assert np.array_equal(csr["col"].cpu().numpy(), nbr[keep])
+    assert np.array_equal(csr["shift"].cpu().numpy(), sh[keep])
+
+
+def test_edge_mask_compaction_long():
+    """The masked path (no nnei) past the one-launch scan size."""
+    rng = np.random.default_rng(11)
+    n, sel = 70001, 5
+    nbr = rng.integers(0, n, size=(n, sel)).astype(np.int32)
+    nbr[rng.random((n, sel)) < 0.3] = -1
+    sh = rng.integers(-1, 2, size=(n, sel, 3)).astype(np.int32)
+    csr = nga.edge_csr(torch.from_numpy(nbr).to(DEV), torch.from_numpy(sh).to(DEV), None)
+    nga.check_status(csr["ws"], "long mask csr")
+    mask = nbr >= 0
+    assert np.array_equal(csr["row_ptr"].cpu().numpy(), np.concatenate([[0], np.cumsum(mask.sum(1))]))
+    assert np.array_equal(csr["col"].cpu().numpy(), nbr[mask])
+
+
 def _expect_status(ws, code):
     assert nga.sync_status(ws) == code
     assert nga.sync_status(ws) == 0  # cleared by the read
