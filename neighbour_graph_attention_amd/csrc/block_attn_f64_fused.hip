@@ -27,6 +27,8 @@
 //                          read from LDS) -> lane (g, l), register r: output 16u+4r+g.
 // Every product's result registers are the next product's operands as they stand; the
 // heads meet once per layer, through LDS, for the output projection.
+#include <type_traits>
+
 #include "block_attn_f64.h"
 
 namespace nga {
@@ -34,6 +36,7 @@ namespace nga {
 namespace {
 
 typedef double d4 __attribute__((ext_vector_type(4)));
+typedef double d2 __attribute__((ext_vector_type(2)));
 
 __device__ inline d4 mfma64(double a, double b, d4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -53,7 +56,24 @@ struct FusedF64Args {
     int nnei_cap;
     int layers;
     uint32_t* status;
+    double one;  // 1.0, a run-time value the compiler cannot fold (settle())
 };
+
+// A matrix-core product's result scaled by f, read first by this vector multiply in the
+// block that issued the product.  The fp64 16x16x4 product writes its result some 19 wait
+// states after issue, and the compiler's hazard pass inserts that wait only along the code
+// as laid out; a later branch that skips a masked region (s_cbranch_execz) can reach the
+// first reader sooner.  That happened here: the row scale's branchy smooth-attention block
+// between the last P.V product and its reader was skipped, and on some boxes the multiply
+// read one of the four result registers before the product had written it (every output
+// row of the last query tile missed the last key group's weighted values).  The empty asm
+// keeps the multiply where it is; every later use, behind whatever branches, reads the
+// multiply's result, which is a plain vector register write.
+__device__ __forceinline__ d4 settle(d4 v, double f) {
+    double a0 = v[0] * f, a1 = v[1] * f, a2 = v[2] * f, a3 = v[3] * f;
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    return d4{a0, a1, a2, a3};
+}
 
 template <int H, int D>
 struct F64Shape {
@@ -62,6 +82,9 @@ struct F64Shape {
     static constexpr int KC = C / 4;        // 4-channel chunks of a contraction over c
     static constexpr int RK = D / 4;        // registers of Q^T / K^T that hold the head
     static constexpr int UO = (C + 15) / 16;  // 16-wide output tiles
+    // A head's O^T tile as the output projection reads it: registers r = 0 .. D/4 - 1 of
+    // each lane (channels 4r + g); heads of 8 leave registers 2 and 3 zero, so they keep two.
+    using OTile = typename std::conditional<D == 8, d2, d4>::type;
 };
 
 // One layer of one centre; rows 16*NT and beyond are absent, rows n .. 16*NT-1 are zero in sX.
@@ -69,7 +92,8 @@ template <int H, int D, int NT>
 __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* __restrict__ W,
                                           const double* __restrict__ ldt, const int64_t r0,
                                           const int n, const bool last, double* __restrict__ sX,
-                                          d4 (*__restrict__ sO)[kFusedF64Tiles][64],
+                                          typename F64Shape<H, D>::OTile (
+                                              *__restrict__ sO)[kFusedF64Tiles][64],
                                           const int lane, const int h) {
     using S = F64Shape<H, D>;
     constexpr int C = S::C, CP = S::CP, KC = S::KC, RK = S::RK, UO = S::UO;
@@ -148,13 +172,10 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
             }
         z += __shfl_xor(z, 16, 64);
         z += __shfl_xor(z, 32, 64);
-        d4 o = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-        for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o = mfma64(v[kt][r], s[kt][r], o);
-        // Smooth attention: sum_j e_j / D~ times the softmax = exp(s_j - ln D~), i.e. the
-        // weighted sum times exp(m - ln D~) in place of 1/Z.
+        // The row's scale, with all of its branches, before the products whose results it
+        // multiplies: see settle() for why no branch may separate those products from their
+        // first reader.  Smooth attention: sum_j e_j / D~ times the softmax =
+        // exp(s_j - ln D~), i.e. the weighted sum times exp(m - ln D~) in place of 1/Z.
         double f = 1.0 / z;
         if (ldt) {
             f = 0.0;
@@ -164,7 +185,14 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
                 if (row >= 0 && row < A.n_edges) f = exp(m * scale - ldt[row * H + h]);
             }
         }
-        sO[h][qt][lane] = o * f;
+        d4 o = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o = mfma64(v[kt][r], s[kt][r], o);
+        o = settle(o, f);
+        if constexpr (D == 8) sO[h][qt][lane] = d2{o[0], o[1]};
+        else sO[h][qt][lane] = o;
     }
     __syncthreads();
 
@@ -180,6 +208,7 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
             const double ov = sO[in / D][qt][lane][(in % D) >> 2];
             acc = mfma64(wo, ov, acc);
         }
+        acc = settle(acc, A.one);
         const int a = 16 * qt + l;
         if (last) {
             if (a < n) {
@@ -204,12 +233,18 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
     }
 }
 
-template <int H, int D>
-__global__ void __launch_bounds__(64 * H, 2) fused_f64_kernel(FusedF64Args A) {
+#ifndef NGA_F64F_MINWG
+#define NGA_F64F_MINWG 2
+#endif
+// NTM: the most 16-row tiles a centre of this launch can have.  Rows of up to 48 leave out
+// the four-tile instance, whose registers would otherwise set the whole kernel's (214 against
+// 166 VGPRs for heads of 8: three work-groups per compute unit instead of two).
+template <int H, int D, int NTM>
+__global__ void __launch_bounds__(64 * H, NGA_F64F_MINWG) fused_f64_kernel(FusedF64Args A) {
     using S = F64Shape<H, D>;
     constexpr int C = S::C, CP = S::CP;
     __shared__ double sX[16 * kFusedF64Tiles * CP];
-    __shared__ d4 sO[H][kFusedF64Tiles][64];
+    __shared__ typename S::OTile sO[H][kFusedF64Tiles][64];
     const int lane = threadIdx.x & 63;
     const int h = threadIdx.x >> 6;
 
@@ -220,7 +255,7 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f64_kernel(FusedF64Args A) {
     const int64_t r0 = A.row_ptr[centre];
     const int64_t r1 = A.row_ptr[centre + 1];
     if (r1 == r0) return;
-    if (r1 < r0 || r1 - r0 > A.nnei_cap || r1 - r0 > 16 * kFusedF64Tiles || r0 < 0 ||
+    if (r1 < r0 || r1 - r0 > A.nnei_cap || r1 - r0 > 16 * NTM || r0 < 0 ||
         r1 > A.n_edges) {
         if (threadIdx.x == 0) raise_bits(A.status, kBitCap);
         return;
@@ -249,7 +284,9 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f64_kernel(FusedF64Args A) {
             case 1: layer_f64<H, D, 1>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
             case 2: layer_f64<H, D, 2>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
             case 3: layer_f64<H, D, 3>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
-            default: layer_f64<H, D, 4>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
+            default:
+                if constexpr (NTM >= 4) layer_f64<H, D, 4>(A, W, ldt, r0, n, last, sX, sO, lane, h);
+                break;
         }
         __syncthreads();
     }
@@ -258,8 +295,12 @@ __global__ void __launch_bounds__(64 * H, 2) fused_f64_kernel(FusedF64Args A) {
 
 template <int H, int D>
 void launch_fused_f64(const FusedF64Args& a, hipStream_t s) {
-    hipLaunchKernelGGL((fused_f64_kernel<H, D>), dim3((unsigned)a.n_centres), dim3(64 * H), 0, s,
-                       a);
+    if (a.nnei_cap <= 48)
+        hipLaunchKernelGGL((fused_f64_kernel<H, D, 3>), dim3((unsigned)a.n_centres), dim3(64 * H),
+                           0, s, a);
+    else
+        hipLaunchKernelGGL((fused_f64_kernel<H, D, 4>), dim3((unsigned)a.n_centres), dim3(64 * H),
+                           0, s, a);
 }
 
 }  // namespace
@@ -287,6 +328,7 @@ int run_fused_f64(const int64_t* row_ptr, const int32_t* order, int64_t n_centre
     a.nnei_cap = nnei_cap;
     a.layers = layers;
     a.status = status;
+    a.one = 1.0;
     const int d = c / heads;
     if (d == 8) {
         switch (heads) {

@@ -170,6 +170,26 @@ def _per_centre_normwise(y, ref, rp):
     return worst
 
 
+@pytest.mark.parametrize("c,heads", [(32, 2), (16, 1), (16, 2), (32, 4)])
+@pytest.mark.parametrize("n", [29, 32, 45, 48, 61, 64])
+def test_fused_f64_every_copy_of_one_centre(oracle_mod, c, heads, n):
+    """2,048 copies of one centre in one fused fp64 launch, each against the oracle.  The
+    rows end in a key group of four with at least one valid key, so the last P.V product of
+    the last query tile contributes; a reader of that product's result scheduled too early
+    (a hazard the kernel guards against) shows up as some copies differing from the rest."""
+    copies = 2048
+    x1 = W.make_features(n, c, 700 + n + c, np.float64)
+    wt = W.make_weights(2, c, 800 + heads, np.float64)
+    assert nga.attn_variant(nga.NGA_F64, 64, c, heads) == "fused_f64"
+    ref = oracle_mod.attn_naive(np.array([0, n], np.int64), x1, wt, heads)
+    rp = (np.arange(copies + 1) * n).astype(np.int64)
+    print(f"c={c} H={heads} n={n} copies={copies}", flush=True)
+    y = _run(rp, np.tile(x1, (copies, 1)), wt, heads, 64)
+    err = np.abs(y.reshape(copies, n, c) - ref[None]).max(axis=(1, 2)) / np.abs(ref).max()
+    bad = np.nonzero(err >= TOL[np.float64])[0]
+    assert len(bad) == 0, f"{len(bad)} copies wrong, worst {err.max():.3e}"
+
+
 @pytest.mark.parametrize("split16", [True, False])
 def test_f32_split_rounding_ties(oracle_mod, split16):
     """fp32 projections on f16 matrix cores take each operand as two f16 parts (hi, lo).  Both
