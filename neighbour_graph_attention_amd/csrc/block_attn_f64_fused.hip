@@ -88,7 +88,9 @@ struct F64Shape {
 };
 
 // One layer of one centre; rows 16*NT and beyond are absent, rows n .. 16*NT-1 are zero in sX.
-template <int H, int D, int NT>
+// SM: smooth attention (ldt given); a separate instance keeps the general exponential and its
+// constants out of the registers of the plain softmax.
+template <int H, int D, int NT, bool SM>
 __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* __restrict__ W,
                                           const double* __restrict__ ldt, const int64_t r0,
                                           const int n, const bool last, double* __restrict__ sX,
@@ -177,7 +179,7 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
         // first reader.  Smooth attention: sum_j e_j / D~ times the softmax =
         // exp(s_j - ln D~), i.e. the weighted sum times exp(m - ln D~) in place of 1/Z.
         double f = 1.0 / z;
-        if (ldt) {
+        if constexpr (SM) {
             f = 0.0;
             const int a = 16 * qt + l;
             if (a < n) {
@@ -239,7 +241,7 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
 // NTM: the most 16-row tiles a centre of this launch can have.  Rows of up to 48 leave out
 // the four-tile instance, whose registers would otherwise set the whole kernel's (214 against
 // 166 VGPRs for heads of 8: three work-groups per compute unit instead of two).
-template <int H, int D, int NTM>
+template <int H, int D, int NTM, bool SM>
 __global__ void __launch_bounds__(64 * H, NGA_F64F_MINWG) fused_f64_kernel(FusedF64Args A) {
     using S = F64Shape<H, D>;
     constexpr int C = S::C, CP = S::CP;
@@ -281,11 +283,12 @@ __global__ void __launch_bounds__(64 * H, NGA_F64F_MINWG) fused_f64_kernel(Fused
         const double* ldt = A.ldt ? A.ldt + (size_t)layer * A.n_edges * H : nullptr;
         const bool last = layer == A.layers - 1;
         switch (nt) {
-            case 1: layer_f64<H, D, 1>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
-            case 2: layer_f64<H, D, 2>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
-            case 3: layer_f64<H, D, 3>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
+            case 1: layer_f64<H, D, 1, SM>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
+            case 2: layer_f64<H, D, 2, SM>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
+            case 3: layer_f64<H, D, 3, SM>(A, W, ldt, r0, n, last, sX, sO, lane, h); break;
             default:
-                if constexpr (NTM >= 4) layer_f64<H, D, 4>(A, W, ldt, r0, n, last, sX, sO, lane, h);
+                if constexpr (NTM >= 4)
+                    layer_f64<H, D, 4, SM>(A, W, ldt, r0, n, last, sX, sO, lane, h);
                 break;
         }
         __syncthreads();
@@ -293,14 +296,20 @@ __global__ void __launch_bounds__(64 * H, NGA_F64F_MINWG) fused_f64_kernel(Fused
     if (bad_index) raise_bits(A.status, kBitIndex);
 }
 
+template <int H, int D, bool SM>
+void launch_fused_f64_sm(const FusedF64Args& a, hipStream_t s) {
+    if (a.nnei_cap <= 48)
+        hipLaunchKernelGGL((fused_f64_kernel<H, D, 3, SM>), dim3((unsigned)a.n_centres),
+                           dim3(64 * H), 0, s, a);
+    else
+        hipLaunchKernelGGL((fused_f64_kernel<H, D, 4, SM>), dim3((unsigned)a.n_centres),
+                           dim3(64 * H), 0, s, a);
+}
+
 template <int H, int D>
 void launch_fused_f64(const FusedF64Args& a, hipStream_t s) {
-    if (a.nnei_cap <= 48)
-        hipLaunchKernelGGL((fused_f64_kernel<H, D, 3>), dim3((unsigned)a.n_centres), dim3(64 * H),
-                           0, s, a);
-    else
-        hipLaunchKernelGGL((fused_f64_kernel<H, D, 4>), dim3((unsigned)a.n_centres), dim3(64 * H),
-                           0, s, a);
+    if (a.ldt) launch_fused_f64_sm<H, D, true>(a, s);
+    else launch_fused_f64_sm<H, D, false>(a, s);
 }
 
 }  // namespace
