@@ -235,14 +235,12 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
     }
 }
 
-#ifndef NGA_F64F_MINWG
-#define NGA_F64F_MINWG 2
-#endif
 // NTM: the most 16-row tiles a centre of this launch can have.  Rows of up to 48 leave out
-// the four-tile instance, whose registers would otherwise set the whole kernel's (214 against
-// 166 VGPRs for heads of 8: three work-groups per compute unit instead of two).
+// the four-tile instance, whose registers would otherwise set the whole kernel's (four heads
+// of 8, plain softmax: 142 instead of 183 VGPRs, three work-groups per compute unit instead
+// of two).
 template <int H, int D, int NTM, bool SM>
-__global__ void __launch_bounds__(64 * H, NGA_F64F_MINWG) fused_f64_kernel(FusedF64Args A) {
+__global__ void __launch_bounds__(64 * H, 2) fused_f64_kernel(FusedF64Args A) {
     using S = F64Shape<H, D>;
     constexpr int C = S::C, CP = S::CP;
     __shared__ double sX[16 * kFusedF64Tiles * CP];
