@@ -170,24 +170,41 @@ def _per_centre_normwise(y, ref, rp):
     return worst
 
 
-@pytest.mark.parametrize("c,heads", [(32, 2), (16, 1), (16, 2), (32, 4)])
-@pytest.mark.parametrize("n", [29, 32, 45, 48, 61, 64])
-def test_fused_f64_every_copy_of_one_centre(oracle_mod, c, heads, n):
-    """2,048 copies of one centre in one fused fp64 launch, each against the oracle.  The
-    rows end in a key group of four with at least one valid key, so the last P.V product of
-    the last query tile contributes; a reader of that product's result scheduled too early
-    (a hazard the kernel guards against) shows up as some copies differing from the rest."""
-    copies = 2048
-    x1 = W.make_features(n, c, 700 + n + c, np.float64)
-    wt = W.make_weights(2, c, 800 + heads, np.float64)
-    assert nga.attn_variant(nga.NGA_F64, 64, c, heads) == "fused_f64"
-    ref = oracle_mod.attn_naive(np.array([0, n], np.int64), x1, wt, heads)
+COPY_CASES = (  # (dtype, c, heads, cap, n, split16, kernel path)
+    [(np.float64, c, h, 64, n, False, "fused_f64") for c, h in [(32, 2), (16, 1), (16, 2), (32, 4)]
+     for n in (29, 32, 45, 48, 61, 64)]
+    + [(np.float64, 128, 4, 128, n, False, "mfma_f64") for n in (61, 120, 128)]
+    + [(np.float32, 64, 4, 192, n, False, "fused_f32") for n in (45, 48, 176, 181, 192)]
+    + [(np.float32, 16, 1, 192, n, False, "fused_f32") for n in (29, 32, 189)]
+    + [(np.float32, 64, 4, 192, n, True, "fused_f32_split16") for n in (48, 181)]
+    + [(np.float32, 40, 5, 64, 61, False, "generic_f32")]
+)
+
+
+@pytest.mark.parametrize("dtype,c,heads,cap,n,split16,variant", COPY_CASES)
+def test_every_copy_of_one_centre(oracle_mod, dtype, c, heads, cap, n, split16, variant):
+    """Many copies of one centre in one launch, each against the oracle.  The rows end in a
+    key group of four with at least one valid key, so the last P.V product of the last query
+    tile contributes; a reader of a matrix-core result scheduled too early, or any other
+    race, shows up as some copies differing from the rest (the fused fp64 kernel once got
+    about 96% of such copies wrong on some GPUs)."""
+    copies = 512 if variant == "mfma_f64" else 2048
+    dt = nga.NGA_F32_SPLIT16 if split16 else (nga.NGA_F64 if dtype == np.float64 else nga.NGA_F32)
+    assert nga.attn_variant(dt, cap, c, heads) == variant
+    x1 = W.make_features(n, c, 700 + n + c, dtype)
+    wt = W.make_weights(2, c, 800 + heads, dtype)
+    ref = oracle_mod.attn_naive(np.array([0, n], np.int64), x1.astype(np.float64),
+                                wt.astype(np.float64), heads)
     rp = (np.arange(copies + 1) * n).astype(np.int64)
-    print(f"c={c} H={heads} n={n} copies={copies}", flush=True)
-    y = _run(rp, np.tile(x1, (copies, 1)), wt, heads, 64)
-    err = np.abs(y.reshape(copies, n, c) - ref[None]).max(axis=(1, 2)) / np.abs(ref).max()
-    bad = np.nonzero(err >= TOL[np.float64])[0]
+    print(f"{variant} c={c} H={heads} n={n} copies={copies}", flush=True)
+    y = _run(rp, np.tile(x1, (copies, 1)), wt, heads, cap, split16=split16)
+    err = (np.abs(y.reshape(copies, n, c).astype(np.float64) - ref[None]).max(axis=(1, 2))
+           / np.abs(ref).max())
+    bad = np.nonzero(err >= TOL[dtype])[0]
     assert len(bad) == 0, f"{len(bad)} copies wrong, worst {err.max():.3e}"
+    # every copy is the same computation: the outputs agree bit for bit
+    y3 = y.reshape(copies, n, c)
+    assert np.array_equal(y3, np.broadcast_to(y3[:1], y3.shape))
 
 
 @pytest.mark.parametrize("split16", [True, False])

@@ -119,6 +119,26 @@ def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, see
     assert np.all(y[0] == 0.0)  # the empty centre
 
 
+@pytest.mark.parametrize("dtype,c,heads,n", [(np.float32, 64, 4, n) for n in (13, 16, 61, 181)]
+                         + [(np.float64, 32, 4, n) for n in (29, 64)] + [(np.float32, 32, 2, 47)])
+def test_every_copy_of_one_centre(oracle_mod, dtype, c, heads, n):
+    """2,048 copies of one centre (same rows, same centre row) in one launch: each against the
+    oracle and all bit-identical, so a race or a result read too early in the streaming pass
+    would show as copies that differ."""
+    copies = 2048
+    x1 = W.make_features(n, c, 900 + n, dtype)
+    xc1 = W.make_features(1, c, 950 + n, dtype)
+    wt = W.make_weights(2, c, 990 + heads, dtype)
+    ref = oracle_mod.local_atten(np.array([0, n], np.int64), xc1.astype(np.float64),
+                                 x1.astype(np.float64), wt.astype(np.float64), heads)
+    rp = (np.arange(copies + 1) * n).astype(np.int64)
+    print(f"{dtype.__name__} c={c} H={heads} n={n} copies={copies}", flush=True)
+    y = _local(rp, np.tile(xc1, (copies, 1)), np.tile(x1, (copies, 1)), wt, heads)
+    err = np.abs(y.astype(np.float64) - ref).max(axis=1) / np.abs(ref).max()
+    assert np.all(err < TOL[dtype]), f"{int(np.sum(err >= TOL[dtype]))} copies wrong"
+    assert np.array_equal(y, np.broadcast_to(y[:1], y.shape))
+
+
 def _first_layer_scores(rp, xc, x, w, heads, i):
     """Scores of centre i's rows in the first layer, [rows][heads], natural units."""
     c = x.shape[1]
