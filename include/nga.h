@@ -238,7 +238,7 @@ size_t edge_csr_workspace_bytes(int64_t n_atoms, int32_t sel);
  * nbr, nbr_shift  [n_atoms][sel], [n_atoms][sel][3] int32: nl_build's
  *                 output, or any padded list.  Slot order is kept.
  * nnei            [n_atoms] int32 or NULL.  When given, the first
- *                 min(nnei[i], sel) slots of row i are its edges (a
+ *                 min(max(nnei[i], 0), sel) slots of row i are its edges (a
  *                 left-packed list) and must hold indices in [0, n_atoms)
  *                 (else NGA_EINDEX).  When NULL, slot k of row i is an edge
  *                 iff nbr >= 0 (the edge mask).
