@@ -162,6 +162,57 @@ def test_random_ragged_rows(oracle_mod, dtype, nc, maxlen, c, heads, layers, see
     assert err < TOL[dtype]
 
 
+def _merged_core_wo(n_centres):
+    """Whether the fp64 matrix-core path (c = 128, heads of 16 or 32) runs the core and the
+    output projection as one work-group per centre: when ceil(n / CUs) rounds of that kernel
+    beat n / CUs rounds of the per-head core and the row GEMM (18 ceil(r) <= 25 r)."""
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    rounds = -(-n_centres // cus)
+    return 18 * rounds * cus <= 25 * n_centres
+
+
+@pytest.mark.parametrize("nc,maxlen,heads,layers,seed,with_order", [
+    (220, 128, 4, 2, 40, False),   # heads of 32, rows up to the 128 cap, one round of CUs
+    (220, 120, 8, 2, 41, False),   # heads of 16
+    (600, 100, 4, 1, 42, False),   # more than one round
+    (220, 128, 4, 2, 43, True),    # rows stored out of slot order (gather and scatter by order)
+])
+def test_f64_merged_core_and_projection(oracle_mod, nc, maxlen, heads, layers, seed, with_order):
+    """fp64, c = 128, enough centres that each centre gets a work-group for all of its heads
+    and the output projection.  Against the oracle, and bit for bit against the same centres
+    run in launches of 20, which take the per-head core and the row GEMM: both sum every
+    output element over the same channel groups in the same order."""
+    c = 128
+    assert nga.attn_variant(nga.NGA_F64, maxlen, c, heads) == "mfma_f64"
+    assert _merged_core_wo(nc) and not _merged_core_wo(20)
+    rp = W.random_rows(nc, maxlen, seed)
+    lens = np.diff(rp)
+    for k, v in enumerate([0, 1, maxlen, 15, 16, 17, 31, 32, 33, 63, 64, 65, 112, 113]):
+        lens[k] = min(v, maxlen)
+    rp = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    e = int(rp[-1])
+    x = W.make_features(e, c, seed + 100, np.float64)
+    wt = W.make_weights(layers, c, seed + 200, np.float64)
+    if with_order:
+        perm = np.random.default_rng(seed + 300).permutation(e).astype(np.int32)
+        x2 = np.empty_like(x)
+        x2[perm] = x
+        y = _run(rp, x2, wt, heads, maxlen, order=perm)[perm]
+    else:
+        y = _run(rp, x, wt, heads, maxlen)
+    ref = oracle_mod.attn_naive(rp, x, wt, heads)
+    err = _normwise(y, ref)
+    print(f"merged core and projection: {nc} centres, H={heads}, L={layers}, E={e}, "
+          f"normwise error {err:.3e}", flush=True)
+    assert err < TOL[np.float64]
+    y_small = np.empty_like(y)
+    for i0 in range(0, nc, 20):
+        i1 = min(nc, i0 + 20)
+        a, b = int(rp[i0]), int(rp[i1])
+        y_small[a:b] = _run(rp[i0:i1 + 1] - a, np.ascontiguousarray(x[a:b]), wt, heads, maxlen)
+    assert np.array_equal(y, y_small)
+
+
 def _per_centre_normwise(y, ref, rp):
     worst = 0.0
     for i in range(rp.shape[0] - 1):
@@ -174,6 +225,7 @@ COPY_CASES = (  # (dtype, c, heads, cap, n, split16, kernel path)
     [(np.float64, c, h, 64, n, False, "fused_f64") for c, h in [(32, 2), (16, 1), (16, 2), (32, 4)]
      for n in (29, 32, 45, 48, 61, 64)]
     + [(np.float64, 128, 4, 128, n, False, "mfma_f64") for n in (61, 120, 128)]
+    + [(np.float64, 128, 8, 128, n, False, "mfma_f64") for n in (61, 128)]
     + [(np.float32, 64, 4, 192, n, False, "fused_f32") for n in (45, 48, 176, 181, 192)]
     + [(np.float32, 16, 1, 192, n, False, "fused_f32") for n in (29, 32, 189)]
     + [(np.float32, 64, 4, 192, n, True, "fused_f32_split16") for n in (48, 181)]
@@ -188,23 +240,24 @@ def test_every_copy_of_one_centre(oracle_mod, dtype, c, heads, cap, n, split16, 
     tile contributes; a reader of a matrix-core result scheduled too early, or any other
     race, shows up as some copies differing from the rest (the fused fp64 kernel once got
     about 96% of such copies wrong on some GPUs)."""
-    copies = 512 if variant == "mfma_f64" else 2048
     dt = nga.NGA_F32_SPLIT16 if split16 else (nga.NGA_F64 if dtype == np.float64 else nga.NGA_F32)
     assert nga.attn_variant(dt, cap, c, heads) == variant
     x1 = W.make_features(n, c, 700 + n + c, dtype)
     wt = W.make_weights(2, c, 800 + heads, dtype)
     ref = oracle_mod.attn_naive(np.array([0, n], np.int64), x1.astype(np.float64),
                                 wt.astype(np.float64), heads)
-    rp = (np.arange(copies + 1) * n).astype(np.int64)
-    print(f"{variant} c={c} H={heads} n={n} copies={copies}", flush=True)
-    y = _run(rp, np.tile(x1, (copies, 1)), wt, heads, cap, split16=split16)
-    err = (np.abs(y.reshape(copies, n, c).astype(np.float64) - ref[None]).max(axis=(1, 2))
-           / np.abs(ref).max())
-    bad = np.nonzero(err >= TOL[dtype])[0]
-    assert len(bad) == 0, f"{len(bad)} copies wrong, worst {err.max():.3e}"
-    # every copy is the same computation: the outputs agree bit for bit
-    y3 = y.reshape(copies, n, c)
-    assert np.array_equal(y3, np.broadcast_to(y3[:1], y3.shape))
+    # fp64 at c = 128: 128 copies take the per-head core, 512 the merged core and projection
+    for copies in ((128, 512) if variant == "mfma_f64" else (2048,)):
+        rp = (np.arange(copies + 1) * n).astype(np.int64)
+        print(f"{variant} c={c} H={heads} n={n} copies={copies}", flush=True)
+        y = _run(rp, np.tile(x1, (copies, 1)), wt, heads, cap, split16=split16)
+        err = (np.abs(y.reshape(copies, n, c).astype(np.float64) - ref[None]).max(axis=(1, 2))
+               / np.abs(ref).max())
+        bad = np.nonzero(err >= TOL[dtype])[0]
+        assert len(bad) == 0, f"{len(bad)} copies wrong, worst {err.max():.3e}"
+        # every copy is the same computation: the outputs agree bit for bit
+        y3 = y.reshape(copies, n, c)
+        assert np.array_equal(y3, np.broadcast_to(y3[:1], y3.shape))
 
 
 @pytest.mark.parametrize("split16", [True, False])

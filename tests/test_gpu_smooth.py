@@ -85,6 +85,8 @@ CASES = [
     (np.float64, 30, 120, 128, 4, 2, 4, "mfma_f64"),
     (np.float64, 40, 40, 32, 4, 2, 5, "fused_f64"),
     (np.float64, 30, 90, 64, 4, 2, 8, "mfma_f64"),
+    (np.float64, 220, 120, 128, 4, 2, 9, "mfma_f64"),   # one work-group per centre, heads of 32
+    (np.float64, 220, 100, 128, 8, 1, 10, "mfma_f64"),  # the same, heads of 16
     (np.float64, 20, 30, 20, 2, 2, 6, "generic_f64"),
     (np.float32, 20, 60, 40, 5, 2, 7, "generic_f32"),
 ]
