@@ -152,12 +152,13 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
             }
             s[kt] = acc;
         }
+        // NT = ceil(n / 16), so only keys of the last tile can lie past n.
         double m = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if (16 * kt + 4 * r + g >= n) s[kt][r] = -INFINITY;
+                if (kt == NT - 1 && 16 * kt + 4 * r + g >= n) s[kt][r] = -INFINITY;
                 m = fmax(m, s[kt][r]);
             }
         m = fmax(m, __shfl_xor(m, 16, 64));
@@ -167,7 +168,7 @@ __device__ __forceinline__ void layer_f64(const FusedF64Args& A, const double* _
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool masked = 16 * kt + 4 * r + g >= n;
+                const bool masked = kt == NT - 1 && 16 * kt + 4 * r + g >= n;
                 const double p = exp2_nonpos(masked ? -4096.0 : (s[kt][r] - m) * scale2);
                 s[kt][r] = p;
                 z += p;
