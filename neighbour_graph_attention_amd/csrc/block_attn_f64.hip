@@ -34,6 +34,16 @@ __device__ inline d4 mfma64(double a, double b, d4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
+// A matrix-core result scaled by f and held in place by an empty asm: every later reader,
+// behind whatever branches, reads this vector multiply's result, never the product's
+// registers themselves (an fp64 product writes them some 19 wait states after issue, and a
+// branch that skips a masked region could otherwise reach a reader sooner).
+__device__ __forceinline__ d4 settle_d4(d4 v, double f) {
+    double a0 = v[0] * f, a1 = v[1] * f, a2 = v[2] * f, a3 = v[3] * f;
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    return d4{a0, a1, a2, a3};
+}
+
 struct GemmF64Args {
     const double* a;
     const int32_t* a_rows;    // nullable: row m of A is a[a_rows[m]]
@@ -47,6 +57,7 @@ struct GemmF64Args {
     int lda;
     int ldo;
     uint32_t* status;
+    double one;  // 1.0, a run-time value the compiler cannot fold (settle_d4)
 };
 
 constexpr int kKc = 16;  // k chunk staged in LDS
@@ -54,8 +65,14 @@ constexpr int kPerB = kKc * 64 / 256;  // values of each B chunk per thread
 
 // out[m][u] = sum_t A[m][t] W_{u / c}[t][u % c]; work-group tile TM x 64, wave w owns rows
 // (TM/2)*(w/2) .. +TM/2 and columns 32*(w%2) .. +32 as (TM/32) x 2 matrix-core tiles.
-template <int TM>
+// C > 0: c is known at compile time and a multiple of 64, so every column and k index is in
+// range, the k loop unrolls and the loads need no guards (rows past E read row 0 and are
+// replaced by zeros); C = 0: any c, checked at run time.
+template <int TM, int C>
 __global__ void __launch_bounds__(256) gemm_f64_kernel(GemmF64Args g) {
+    static_assert(C % 64 == 0, "compile-time widths are multiples of 64");
+    constexpr bool kFixed = C > 0;
+    const int c = kFixed ? C : g.c;
     constexpr int PA = TM * kKc / 256;  // values of each A chunk per thread
     constexpr int BI = TM / 32;         // 16-row matrix-core tiles per wave
     __shared__ double sA[TM][kKc + 1];
@@ -64,7 +81,7 @@ __global__ void __launch_bounds__(256) gemm_f64_kernel(GemmF64Args g) {
     const int64_t m0 = (int64_t)blockIdx.x * TM;
     const int u0 = blockIdx.y * 64;
     if (m0 >= E) return;
-    const int nout = g.nmat * g.c;
+    const int nout = g.nmat * c;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int gq = lane >> 4, li = lane & 15;
     const int wr = (TM / 2) * (w >> 1), wc = 32 * (w & 1);
@@ -93,22 +110,33 @@ __global__ void __launch_bounds__(256) gemm_f64_kernel(GemmF64Args g) {
         }
     }
     const int u = u0 + tid % 64;
-    const bool u_in = u < nout;
-    const double* wcol = g.w + (u_in ? (int64_t)(u / g.c) * g.c * g.c + (u % g.c) : 0);
+    const bool u_in = kFixed || u < nout;
+    const double* wcol = g.w + (u_in ? (int64_t)(u / c) * c * c + (u % c) : 0);
     double pa[PA], pb[kPerB];
     auto fetch = [&](int k0) {
-        const bool a_k_in = k0 + a_kk < g.c;
+        if constexpr (kFixed) {
 #pragma unroll
-        for (int j = 0; j < PA; ++j)
-            pa[j] = (a_off[j] >= 0 && a_k_in) ? g.a[a_off[j] + k0 + a_kk] : 0.0;
+            for (int j = 0; j < PA; ++j) {
+                const double v = g.a[(a_off[j] >= 0 ? a_off[j] : 0) + k0 + a_kk];
+                pa[j] = a_off[j] >= 0 ? v : 0.0;
+            }
 #pragma unroll
-        for (int j = 0; j < kPerB; ++j) {
-            const int t = k0 + b_k + 4 * j;
-            pb[j] = (u_in && t < g.c) ? wcol[(int64_t)t * g.c] : 0.0;
+            for (int j = 0; j < kPerB; ++j) pb[j] = wcol[(int64_t)(k0 + b_k + 4 * j) * C];
+        } else {
+            const bool a_k_in = k0 + a_kk < c;
+#pragma unroll
+            for (int j = 0; j < PA; ++j)
+                pa[j] = (a_off[j] >= 0 && a_k_in) ? g.a[a_off[j] + k0 + a_kk] : 0.0;
+#pragma unroll
+            for (int j = 0; j < kPerB; ++j) {
+                const int t = k0 + b_k + 4 * j;
+                pb[j] = (u_in && t < c) ? wcol[(int64_t)t * c] : 0.0;
+            }
         }
     };
-    fetch(0);
-    for (int k0 = 0; k0 < g.c; k0 += kKc) {
+    // One k chunk: the staged chunk from registers into LDS, the next chunk's loads, the
+    // chunk's products.
+    auto chunk = [&](int k0) {
 #pragma unroll
         for (int j = 0; j < PA; ++j) {
             const int idx = tid + 256 * j;
@@ -120,7 +148,7 @@ __global__ void __launch_bounds__(256) gemm_f64_kernel(GemmF64Args g) {
             sB[idx / 64][idx % 64] = pb[j];
         }
         __syncthreads();
-        if (k0 + kKc < g.c) fetch(k0 + kKc);
+        if (k0 + kKc < c) fetch(k0 + kKc);
 #pragma unroll
         for (int ks = 0; ks < kKc / 4; ++ks) {
             double a[BI], b[2];
@@ -134,7 +162,20 @@ __global__ void __launch_bounds__(256) gemm_f64_kernel(GemmF64Args g) {
                 for (int j = 0; j < 2; ++j) acc[i][j] = mfma64(a[i], b[j], acc[i][j]);
         }
         __syncthreads();
+    };
+    fetch(0);
+    if constexpr (kFixed) {
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += kKc) chunk(k0);
+    } else {
+        for (int k0 = 0; k0 < c; k0 += kKc) chunk(k0);
     }
+    // The stores below sit behind row and index branches: they read the products' results
+    // through this multiply (see settle_d4).
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = settle_d4(acc[i][j], g.one);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
 #pragma unroll
@@ -149,7 +190,7 @@ __global__ void __launch_bounds__(256) gemm_f64_kernel(GemmF64Args g) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int u = u0 + wc + 16 * j + li;
-                if (u < nout) g.out[row * g.ldo + u] = acc[i][j][r];
+                if (kFixed || u < nout) g.out[row * g.ldo + u] = acc[i][j][r];
             }
         }
     if (bad) raise_bits(g.status, kBitIndex);
@@ -352,16 +393,6 @@ struct CoreWoF64Args {
     uint32_t* status;
     double one;                 // 1.0, a run-time value the compiler cannot fold (settle_d4)
 };
-
-// A matrix-core result scaled by f and held in place by an empty asm: every later reader,
-// behind whatever branches, reads this vector multiply's result, never the product's
-// registers themselves (an fp64 product writes them some 19 wait states after issue, and a
-// branch that skips a masked region could otherwise reach a reader sooner).
-__device__ __forceinline__ d4 settle_d4(d4 v, double f) {
-    double a0 = v[0] * f, a1 = v[1] * f, a2 = v[2] * f, a3 = v[3] * f;
-    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
-    return d4{a0, a1, a2, a3};
-}
 
 template <int D, int C, int NT, bool SM>
 __device__ __forceinline__ void core_wo_centre(const CoreWoF64Args& A,
@@ -633,7 +664,9 @@ int launch_gemm(const GemmF64Args& g, int64_t m_bound, hipStream_t s) {
     constexpr int TM = kGemmRows;
     const int nout = g.nmat * g.c;
     dim3 grid((unsigned)((m_bound + TM - 1) / TM), (unsigned)((nout + 63) / 64));
-    hipLaunchKernelGGL(gemm_f64_kernel<TM>, grid, dim3(256), 0, s, g);
+    if (g.c == 128) hipLaunchKernelGGL((gemm_f64_kernel<TM, 128>), grid, dim3(256), 0, s, g);
+    else if (g.c == 64) hipLaunchKernelGGL((gemm_f64_kernel<TM, 64>), grid, dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((gemm_f64_kernel<TM, 0>), grid, dim3(256), 0, s, g);
     return last_launch_status();
 }
 
@@ -677,6 +710,7 @@ int run_f64_mfma(const int64_t* row_ptr, const int32_t* order, int64_t n_centres
         g1.lda = c;
         g1.ldo = 3 * c;
         g1.status = status;
+        g1.one = 1.0;
         if ((rc = launch_gemm(g1, n_edges, s))) return rc;
         CoreF64Args a;
         a.qkv = qkv;
