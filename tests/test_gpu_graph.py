@@ -26,7 +26,7 @@ def _eager(pos, box, w, x, wt):
     return nbr, nnei, csr, y
 
 
-@pytest.mark.parametrize("key", [1, 4])
+@pytest.mark.parametrize("key", [1, 2, 4])  # 2: the merged fp64 core and projection
 def test_replays_equal_eager_steps(key):
     w = W.WORKLOADS[key]
     pos_np, box = W.workload_positions(w)
