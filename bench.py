@@ -576,7 +576,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "n_atoms": n, "n_edges": e, "rcut": w.rcut, "sel": w.sel,
                    "channels": w.c, "heads": w.heads, "layers": w.layers,
-                   "geometry_dtype": "f64", "attn_kernel": variant},
+                   "geometry_dtype": "f64", "attn_kernel": variant,
+                   "attn_plan": nga.attn_plan(dtype_code, n, w.sel, w.c, w.heads)},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic,
                      "kernel": variant, "flops_per_launch": flops, "launch_ms": attn_ms,

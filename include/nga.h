@@ -496,6 +496,20 @@ const char* nga_strerror(int status);
  * cover. */
 const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, int32_t n_heads);
 
+/* The same, with the layer plan of the fp64 matrix-core path for n_centres
+ * centres on the current device, for reporting and tests: "mfma_f64.merged"
+ * (per layer a row GEMM for Q, K and V, then one work-group per centre for the
+ * attention core and the output projection together: c = 128, heads of 16 or
+ * 32, when ceil(n/CUs) rounds of that kernel beat n/CUs rounds of the other
+ * plan, 18 ceil(n/CUs) <= 25 n/CUs) or "mfma_f64.per_head" (a row GEMM, the
+ * core per (centre, head), a row GEMM for the output projection); both give
+ * bit-identical outputs.  Other shapes: nga_attn_variant's name.  Reads the
+ * current device's compute-unit count once per device; never NULL.  deepmd-kit
+ * issue "perf: NeighborGraph attention is 4-9x slower than dense ...", section
+ * "Proposed fix: block-dense attention on the graph". */
+const char* nga_attn_plan(int dtype, int64_t n_centres, int32_t nnei_cap, int32_t c,
+                          int32_t n_heads);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     NGAError,
     StepGraph,
     Workspace,
+    attn_plan,
     attn_variant,
     block_attn_forward,
     block_attn_workspace_bytes,

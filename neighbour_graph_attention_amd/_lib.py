@@ -24,7 +24,7 @@ ROW_CAP = 512
 
 EXPORTS = ("nl_build_workspace_bytes", "nl_build", "edge_csr_workspace_bytes", "edge_csr",
            "block_attn_workspace_bytes", "block_attn_forward", "nga_sync_status", "nga_strerror",
-           "nga_attn_variant", "pair_attn_workspace_bytes", "pair_attn_forward",
+           "nga_attn_variant", "nga_attn_plan", "pair_attn_workspace_bytes", "pair_attn_forward",
            "block_attn_forward_smooth", "local_attn_workspace_bytes", "local_attn_forward",
            "nga_step_graph_create", "nga_step_graph_launch", "nga_step_graph_destroy",
            "nl_refine", "nl_max_displacement", "nl_build_batch_workspace_bytes",
@@ -104,6 +104,8 @@ def load() -> ctypes.CDLL:
     lib.nga_strerror.argtypes = [ctypes.c_int]
     lib.nga_attn_variant.restype = ctypes.c_char_p
     lib.nga_attn_variant.argtypes = [ctypes.c_int, i32, i32, i32]
+    lib.nga_attn_plan.restype = ctypes.c_char_p
+    lib.nga_attn_plan.argtypes = [ctypes.c_int, i64, i32, i32, i32]
     _lib = lib
     return lib
 
@@ -313,6 +315,12 @@ def block_attn_workspace_bytes(dtype: int, n_edges: int, nnei_cap: int, c: int, 
 
 def attn_variant(dtype: int, nnei_cap: int, c: int, n_heads: int) -> str:
     return load().nga_attn_variant(dtype, nnei_cap, c, n_heads).decode()
+
+
+def attn_plan(dtype: int, n_centres: int, nnei_cap: int, c: int, n_heads: int) -> str:
+    """nga_attn_plan: the variant name, with the fp64 matrix-core path's layer plan for this
+    many centres on the current device ("mfma_f64.merged" or "mfma_f64.per_head")."""
+    return load().nga_attn_plan(dtype, int(n_centres), nnei_cap, c, n_heads).decode()
 
 
 def block_attn_forward(row_ptr: torch.Tensor, x: torch.Tensor, weights: torch.Tensor,

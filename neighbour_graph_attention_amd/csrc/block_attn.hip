@@ -270,6 +270,24 @@ extern "C" const char* nga_attn_variant(int dtype, int32_t nnei_cap, int32_t c, 
 }
 
 namespace nga {
+// block_attn_f64.hip: true if the fp64 matrix-core path runs the attention core and the output
+// projection as one work-group per centre (c = 128, heads of 16 or 32, enough centres to fill
+// the current device's compute units in every round) rather than per (centre, head) followed
+// by a row GEMM.
+bool f64_core_wo_selected(int64_t n_centres, int32_t c, int32_t heads);
+}  // namespace nga
+
+extern "C" const char* nga_attn_plan(int dtype, int64_t n_centres, int32_t nnei_cap, int32_t c,
+                                     int32_t n_heads) {
+    const char* v = nga_attn_variant(dtype, nnei_cap, c, n_heads);
+    if (dtype == NGA_F64 && nga::f64_mfma_supported(nnei_cap, c, n_heads) &&
+        !nga::fused_f64_supported(nnei_cap, c, n_heads))
+        return nga::f64_core_wo_selected(n_centres, c, n_heads) ? "mfma_f64.merged"
+                                                                : "mfma_f64.per_head";
+    return v;
+}
+
+namespace nga {
 namespace {
 
 int attn_forward(int dtype, const int64_t* row_ptr, const int32_t* order, int64_t n_centres,

@@ -680,6 +680,11 @@ int launch_core(const CoreF64Args& a, int64_t n_centres, int heads, int d, hipSt
 
 }  // namespace
 
+bool f64_core_wo_selected(int64_t n_centres, int32_t c, int32_t heads) {
+    return heads >= 1 && c % heads == 0 && core_wo_supported(c, c / heads) &&
+           use_core_wo(n_centres);
+}
+
 bool f64_mfma_supported(int32_t nnei_cap, int32_t c, int32_t heads) {
     if (heads < 1 || c % heads != 0) return false;
     const int d = c / heads;
@@ -725,7 +730,7 @@ int run_f64_mfma(const int64_t* row_ptr, const int32_t* order, int64_t n_centres
         a.order = order;
         a.status = status;
         const bool last = (l == layers - 1);
-        if (core_wo_supported(c, d) && use_core_wo(n_centres)) {
+        if (f64_core_wo_selected(n_centres, c, heads)) {
             CoreWoF64Args b;
             b.qkv = qkv;
             b.wo = W + 3 * cc;

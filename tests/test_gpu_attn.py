@@ -185,6 +185,8 @@ def test_f64_merged_core_and_projection(oracle_mod, nc, maxlen, heads, layers, s
     c = 128
     assert nga.attn_variant(nga.NGA_F64, maxlen, c, heads) == "mfma_f64"
     assert _merged_core_wo(nc) and not _merged_core_wo(20)
+    assert nga.attn_plan(nga.NGA_F64, nc, maxlen, c, heads) == "mfma_f64.merged"
+    assert nga.attn_plan(nga.NGA_F64, 20, maxlen, c, heads) == "mfma_f64.per_head"
     rp = W.random_rows(nc, maxlen, seed)
     lens = np.diff(rp)
     for k, v in enumerate([0, 1, maxlen, 15, 16, 17, 31, 32, 33, 63, 64, 65, 112, 113]):
@@ -248,6 +250,9 @@ def test_every_copy_of_one_centre(oracle_mod, dtype, c, heads, cap, n, split16, 
                                 wt.astype(np.float64), heads)
     # fp64 at c = 128: 128 copies take the per-head core, 512 the merged core and projection
     for copies in ((128, 512) if variant == "mfma_f64" else (2048,)):
+        if variant == "mfma_f64":
+            assert nga.attn_plan(dt, copies, cap, c, heads) == (
+                "mfma_f64.merged" if copies == 512 else "mfma_f64.per_head")
         rp = (np.arange(copies + 1) * n).astype(np.int64)
         print(f"{variant} c={c} H={heads} n={n} copies={copies}", flush=True)
         y = _run(rp, np.tile(x1, (copies, 1)), wt, heads, cap, split16=split16)
