@@ -171,6 +171,39 @@ def _merged_core_wo(n_centres):
     return 18 * rounds * cus <= 25 * n_centres
 
 
+def test_f64_layer_plan_follows_its_rule():
+    """The plan the library picks for c = 128 equals the rule, at every centre count up to
+    three rounds of compute units, for heads of 32 and 16; heads of 8 and other widths always
+    take the per-head core."""
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    for n in range(1, 3 * cus + 2):
+        want = "mfma_f64.merged" if _merged_core_wo(n) else "mfma_f64.per_head"
+        for heads in (4, 8):
+            assert nga.attn_plan(nga.NGA_F64, n, 128, 128, heads) == want, (n, heads)
+        assert nga.attn_plan(nga.NGA_F64, n, 128, 128, 16) == "mfma_f64.per_head"
+        assert nga.attn_plan(nga.NGA_F64, n, 128, 64, 2) == "mfma_f64.per_head"
+    assert nga.attn_plan(nga.NGA_F64, 1000, 40, 32, 4) == "fused_f64"
+    assert nga.attn_plan(nga.NGA_F32, 1000, 181, 64, 4) == "fused_f32"
+
+
+@pytest.mark.parametrize("side", [0, 1])
+def test_f64_plans_either_side_of_the_switch(oracle_mod, side):
+    """The smallest centre count that takes the merged kernel, and the one below it: both
+    against the oracle, on short ragged rows."""
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    first = next(n for n in range(1, 2 * cus) if _merged_core_wo(n))
+    nc = first - 1 + side
+    assert nga.attn_plan(nga.NGA_F64, nc, 40, 128, 4) == (
+        "mfma_f64.merged" if side else "mfma_f64.per_head")
+    rp = W.random_rows(nc, 40, 60 + side, min_len=1)
+    e = int(rp[-1])
+    x = W.make_features(e, 128, 61 + side, np.float64)
+    wt = W.make_weights(2, 128, 62 + side, np.float64)
+    y = _run(rp, x, wt, 4, 40)
+    ref = oracle_mod.attn_naive(rp, x, wt, 4)
+    assert _normwise(y, ref) < TOL[np.float64]
+
+
 @pytest.mark.parametrize("nc,maxlen,heads,layers,seed,with_order", [
     (220, 128, 4, 2, 40, False),   # heads of 32, rows up to the 128 cap, one round of CUs
     (220, 120, 8, 2, 41, False),   # heads of 16
